@@ -1,0 +1,140 @@
+"""Block summarizer, block-score estimator and tile selection (oracle).
+
+Follows, in order, the dynamic-mask steps of the SPADE review page:
+  1. summarize each block by the mean of its Q and of its K vectors
+     (MEAN summarizer: "Axiom & Free-Parameter Ledger", the summarizer /
+     estimator axiom, and Figure 4);
+  2. estimate block importance by the product of the summaries
+     ("What carries the argument": Summarizer/Estimator expressions);
+  3. keep, per query tile, the key tiles passing a Top-K or Top-P filter
+     together with a local window ("Core claim": Top-K/Top-P and
+     local-window filter; thresholds have no values on the page, see the
+     ledger's free parameters).
+The kept pairs form the block mask M of the referee report's minor
+comment on Eq. (2): 0 on kept block pairs, -inf on pruned ones.
+
+Arithmetic fixed here so that an independent implementation reaches the
+same integers:
+  * pooled mean: exact sum of the bf16 values (asserted exact in fp64),
+    one fp64 division by the token count, one rounding to fp32;
+  * tile score S_ij = fl64(scale * acc) where acc adds the fp64 products
+    q_i[c] * k_j[c] (exact: fp32 x fp32 fits in fp64) left to right over
+    c = 0..d-1 starting from 0;
+  * ties between equal scores go to the lower key-tile index.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import geometry
+
+
+def default_scale(d):
+    """Softmax scale 1/sqrt(d) in fp64."""
+    return 1.0 / math.sqrt(float(d))
+
+
+def _assert_exact_sum(x):
+    """Every partial sum of x (fp64) is exact, whatever the order.
+
+    x holds bf16 values (8 significant bits).  All of them are multiples of
+    2^e_lo (e_lo = exponent of the smallest one's last bit), so if
+    sum(|x|) < 2^(e_lo + 53) every partial sum is representable.
+    """
+    nz = x[x != 0]
+    if nz.size == 0:
+        return
+    _, e = np.frexp(np.abs(nz))          # |v| in [2^(e-1), 2^e)
+    e_lo = int(e.min()) - 1 - 7          # last bit of an 8-bit significand
+    total = float(np.abs(nz).sum())
+    assert total < math.ldexp(1.0, e_lo + 53), "pooled sum not exact in fp64"
+
+
+def pooled_means(x, members):
+    """Mean vector of each tile: x [N, d] (bf16 values) -> fp32 [nT, d]."""
+    x64 = np.asarray(x, dtype=np.float64)
+    out = np.zeros((len(members), x64.shape[1]), dtype=np.float32)
+    for i, m in enumerate(members):
+        blk = x64[m]
+        _assert_exact_sum(blk)
+        s = blk.sum(axis=0)                       # exact, order-free
+        out[i] = (s / float(len(m))).astype(np.float32)
+    return out
+
+
+def tile_scores(pq, pk, scale):
+    """S[i, j] = scale * <pq_i, pk_j>, fixed left-to-right fp64 order."""
+    pq64 = np.asarray(pq, dtype=np.float64)
+    pk64 = np.asarray(pk, dtype=np.float64)
+    acc = np.zeros((pq64.shape[0], pk64.shape[0]), dtype=np.float64)
+    for c in range(pq64.shape[1]):
+        acc = acc + np.outer(pq64[:, c], pk64[:, c])
+    return acc * float(scale)
+
+
+def frac_count(frac, n):
+    """Number of items that make up fraction frac of n, rounded up.
+
+    The 1e-9 slack keeps a product that is an integer in exact arithmetic
+    (0.2 * 315 = 63) from being bumped up by its fp64 representation.
+    """
+    return max(1, int(math.ceil(frac * n - 1e-9)))
+
+
+def topk(row, k):
+    """Indices of the k largest entries of row (ties: lower index first)."""
+    order = np.argsort(-row, kind="stable")
+    return sorted(int(j) for j in order[:k])
+
+
+def topp(row, p):
+    """Smallest high-score prefix whose softmax mass reaches p.
+
+    Returns (indices, margin): margin is the distance of the cumulative
+    mass at the cut (and just before it) from p; rows with a tiny margin
+    may legitimately differ between implementations whose exp differs in
+    the last ulp.
+    """
+    e = np.exp(row - row.max())
+    prob = e / e.sum()
+    order = np.argsort(-row, kind="stable")
+    cum = np.cumsum(prob[order])
+    hit = np.nonzero(cum >= p)[0]
+    m = int(hit[0]) if hit.size else len(row) - 1
+    before = cum[m - 1] if m > 0 else 0.0
+    margin = min(abs(cum[m] - p), abs(p - before))
+    return sorted(int(j) for j in order[:m + 1]), float(margin)
+
+
+def select_rows(S, ntiles, window=None, win_mode="truncate", k=0, p=0.0):
+    """Per query tile: window(i) U TopK(i) U TopP(i), sorted ascending.
+
+    S is the [nT, nT] score matrix (may be None when only the window is
+    used).  Returns (rows, margins) where margins holds the Top-P margin
+    per row (inf when Top-P is off).
+    """
+    nT = int(np.prod(ntiles))
+    rows, margins = [], []
+    for i in range(nT):
+        keep = set()
+        if window is not None:
+            keep.update(geometry.window(i, ntiles, window, win_mode))
+        margin = math.inf
+        if k > 0:
+            keep.update(topk(S[i], k))
+        if p > 0.0:
+            idx, margin = topp(S[i], p)
+            keep.update(idx)
+        rows.append(sorted(keep))
+        margins.append(margin)
+    return rows, margins
+
+
+def to_csr(rows):
+    """List of sorted rows -> (row_ptr int32, col_idx int32)."""
+    row_ptr = np.zeros(len(rows) + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int32)
+    return row_ptr, col_idx
