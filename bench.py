@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark: block-sparse video attention on one MI355X.
+
+One step = one vsa_forward call (layout -> selection -> attention) over the
+whole workload, inputs already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config hunyuan]
+
+The headline workload is the HunyuanVideo 720p attention shape (B=1, H=24,
+N=30x48x80=115200, d=128, tiles 6x8x8, sliding tile window 3x3x5).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("ms/attention call + effective TFLOP/s on retained blocks, "
+          "HunyuanVideo-720p shape")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ATTN_SOURCES = ["block_sparse_attention_tile_amd/csrc/attend.hip"]
+
+
+def _src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data[kernel_key][workload]
+    except (KeyError, ValueError):
+        return None
+    if ent.get("source_hash") != _src_hash(ATTN_SOURCES):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def _cpu_baseline(wl, q, k, v, plan, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import attention, geometry
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    row_ptr, col, _ = plan.read_selection()
+    mt = plan.info.max_tiles
+    nT = plan.info.n_tiles[0]
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    h = 0
+    rows = [col[row_ptr[h * mt + i]:row_ptr[h * mt + i + 1]].tolist() for i in range(nT)]
+    qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
+    order = np.random.default_rng(0).permutation(nT)
+    done, flops = [], 0.0
+    t0 = time.perf_counter()
+    for i in order:
+        attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=[int(i)])
+        done.append(int(i))
+        flops += 4.0 * wl.d * len(mem[i]) * sum(len(mem[j]) for j in rows[i])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0, {len(done)} of {nT} query tiles ({len(done) * len(mem[0])} "
+                      f"query rows), fp64 numpy masked-softmax attention; "
+                      f"{dt:.1f} s; {flops:.3e} retained FLOPs",
+            "ms_per_call_extrapolated": dt / flops * plan_total_flops(plan) * 1e3}
+
+
+def plan_total_flops(plan):
+    return plan._retained_flops
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="hunyuan")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_tile_amd as vsa
+    from synth import CONFIGS, smooth_field_qkv
+    from tests.helpers import structs_of
+
+    wl = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=0,
+                               device="cuda")
+    o = torch.empty_like(q)
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    plan.workspace()
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        plan.forward(q, k, v, o)
+    torch.cuda.synchronize()
+    pairs, flops = plan.retained_work()
+    plan._retained_flops = flops
+
+    # ---- timed region: exactly `steps` whole calls
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.forward(q, k, v, o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} calls: {ms:.3f} ms/call", file=sys.stderr, flush=True)
+
+    # ---- per-stage times (same stream, HIP events around each stage)
+    def stage(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n_st = max(5, args.steps)
+    ms_layout = stage(lambda: plan.layout(q, k, v), n_st)
+    ms_select = stage(lambda: plan.select(q, k, v), n_st)
+    ms_attend = stage(lambda: plan.attend(o, q, k, v), n_st)
+
+    BH = wl.B * wl.H
+    bytes_layout = 6.0 * BH * wl.N * wl.d * 2          # read Q,K,V + write tile-major copies
+    attn_tflops = flops / (ms_attend * 1e-3) / 1e12
+    traffic = _traffic("attend", wl.name)
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(wl, q, k, v, plan, args.cpu_budget)
+
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} N={wl.N} "
+                               f"({wl.grid[0]}x{wl.grid[1]}x{wl.grid[2]}) d={wl.d} "
+                               f"tile {wl.tile[0]}x{wl.tile[1]}x{wl.tile[2]}",
+                   "mask": _mask_desc(wl), "retained_pairs": pairs,
+                   "retained_flops": flops, "parallelism": "single GPU"},
+        "stages_ms": {"layout": round(ms_layout, 4), "select": round(ms_select, 4),
+                      "attend": round(ms_attend, 4)},
+        "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1),
+        "layout_hbm_frac": round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "attend_tflops": round(attn_tflops, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def _mask_desc(wl):
+    parts = []
+    if wl.window:
+        parts.append(f"window {wl.window[0]}x{wl.window[1]}x{wl.window[2]} tiles ({wl.win_mode})")
+    if wl.topk:
+        parts.append(f"top-{wl.topk}")
+    if wl.topk_frac:
+        parts.append(f"top-k {wl.topk_frac:.0%} of tiles")
+    if wl.topp:
+        parts.append(f"top-p {wl.topp}")
+    if wl.candidates:
+        parts.append("SICS blocking choice per head")
+    if wl.fine_group:
+        parts.append(f"fine M={wl.fine_group} keep {wl.fine_keep:.0%}")
+    return ", ".join(parts) or "dense"
+
+
+if __name__ == "__main__":
+    main()

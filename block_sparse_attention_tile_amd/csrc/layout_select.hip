@@ -1,0 +1,360 @@
+// Tile layout transform (raster <-> tile-major), pooled tile means, and the
+// tile selection (window / Top-K / Top-P) that produces the kept key tiles of
+// every query tile.
+//
+// Tile geometry: the T x H x W token grid is cut into tiles of tt x th x tw
+// tokens; a tile is one attention block and its tokens stay consecutive
+// (Sliding Tile Attention verdict page, pith_extraction.key_machinery).
+// Tiles are numbered in raster order of tile coordinates; inside a tile the
+// valid tokens keep raster order and the padded slots (edge tiles, and the
+// rounding of the tile size up to 32) come last and are zero.
+//
+// Selection follows the SPADE review page: mean summaries of Q and K per
+// block (Figure 4, MEAN summarizer), block score = product of the summaries,
+// and a Top-K / Top-P filter united with a local window ("Core claim").
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kLayoutThreads = 256;
+constexpr int kChunk = 64;  // slots per layout step
+
+struct TileRef {
+  int it, ih, iw;  // tile coordinates
+  int et, eh, ew;  // extents inside the grid
+  int nvalid;
+};
+
+__device__ __forceinline__ TileRef tile_ref(const Geo& g, const BlkGeo& b, int i) {
+  TileRef t;
+  t.it = i / (b.nt[1] * b.nt[2]);
+  t.ih = (i / b.nt[2]) % b.nt[1];
+  t.iw = i % b.nt[2];
+  t.et = min(b.tile[0], g.grid[0] - t.it * b.tile[0]);
+  t.eh = min(b.tile[1], g.grid[1] - t.ih * b.tile[1]);
+  t.ew = min(b.tile[2], g.grid[2] - t.iw * b.tile[2]);
+  t.nvalid = t.et * t.eh * t.ew;
+  return t;
+}
+
+// Raster token of valid slot s (< nvalid) of tile t.
+__device__ __forceinline__ long token_of(const Geo& g, const BlkGeo& b, const TileRef& t, int s) {
+  const int ehw = t.eh * t.ew;
+  const int st = s / ehw;
+  const int r = s - st * ehw;
+  const int sh = r / t.ew;
+  const int sw = r - sh * t.ew;
+  return ((long)(t.it * b.tile[0] + st) * g.grid[1] + (t.ih * b.tile[1] + sh)) * g.grid[2] +
+         (t.iw * b.tile[2] + sw);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One workgroup per (head, tile): copies Q and K rows to tile-major order,
+// writes V transposed per tile ([d][slots]) through LDS, and optionally the
+// exact per-tile means of Q and K (fp64 sums of bf16 values, one rounding).
+template <int D>
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
+    Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ qt, uint16_t* __restrict__ kt,
+    uint16_t* __restrict__ vt, float* __restrict__ pooled_q, float* __restrict__ pooled_k,
+    const int* __restrict__ cand, int pool) {
+  constexpr int P = D / 8;                    // 16-byte pieces per row
+  constexpr int RPP = kLayoutThreads / P;     // rows per pass
+  __shared__ uint32_t lv[kChunk][D / 2 + 1];  // V chunk, odd row stride: no bank conflicts
+  __shared__ double red[kLayoutThreads][8];
+
+  const int i = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int c = cand ? cand[bh] : 0;
+  const BlkGeo b = pick_blk(g, c);
+  if (i >= b.n_tiles) return;
+  const TileRef t = tile_ref(g, b, i);
+  const int tid = threadIdx.x;
+  const int p = tid % P;
+  const int r0 = tid / P;
+  const long in_base = bh * (long)g.N * D;
+  const long tm_base = bh * g.tok_cap * D + (long)i * b.slots * D;
+
+  double sq[8], sk[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) sq[x] = sk[x] = 0.0;
+
+  for (int s0 = 0; s0 < b.slots; s0 += kChunk) {
+    for (int rr = r0; rr < kChunk; rr += RPP) {
+      const int s = s0 + rr;
+      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
+      if (s < t.nvalid) {
+        const long off = in_base + token_of(g, b, t, s) * D + p * 8;
+        qv = *reinterpret_cast<const uint4*>(q + off);
+        kv = *reinterpret_cast<const uint4*>(k + off);
+        vv = *reinterpret_cast<const uint4*>(v + off);
+      }
+      if (s < b.slots) {
+        *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv;
+        *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv;
+      }
+      if (pool) {
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          sq[2 * x] += (double)bf16_lo(qw[x]);
+          sq[2 * x + 1] += (double)bf16_hi(qw[x]);
+          sk[2 * x] += (double)bf16_lo(kw[x]);
+          sk[2 * x + 1] += (double)bf16_hi(kw[x]);
+        }
+      }
+      lv[rr][p * 4 + 0] = vv.x;
+      lv[rr][p * 4 + 1] = vv.y;
+      lv[rr][p * 4 + 2] = vv.z;
+      lv[rr][p * 4 + 3] = vv.w;
+    }
+    __syncthreads();
+    // V^T pieces: 8 consecutive slots of one channel row; 8 lanes cover a
+    // 128-byte run of the row.
+    const long vt_base = bh * g.tok_cap * D + (long)i * D * b.slots;
+    for (int pc = tid; pc < D * (kChunk / 8); pc += kLayoutThreads) {
+      const int s8 = pc % (kChunk / 8);
+      const int dd = pc / (kChunk / 8);
+      const int sl = s0 + s8 * 8;
+      if (sl >= b.slots) continue;
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t wv = lv[s8 * 8 + j][dd >> 1];
+        h[j] = (dd & 1) ? (wv >> 16) : (wv & 0xffffu);
+      }
+      uint4 out;
+      out.x = h[0] | (h[1] << 16);
+      out.y = h[2] | (h[3] << 16);
+      out.z = h[4] | (h[5] << 16);
+      out.w = h[6] | (h[7] << 16);
+      *reinterpret_cast<uint4*>(vt + vt_base + (long)dd * b.slots + sl) = out;
+    }
+    __syncthreads();
+  }
+
+  if (!pool) return;
+  // Exact sums: every partial sum of bf16 values of moderate range is exact
+  // in fp64, so the reduction order does not change the result.
+  for (int which = 0; which < 2; ++which) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) red[tid][x] = which ? sk[x] : sq[x];
+    __syncthreads();
+    if (tid < D) {
+      const int pp = tid / 8, xx = tid % 8;
+      double s = 0.0;
+      for (int r = 0; r < RPP; ++r) s += red[r * P + pp][xx];
+      float* dst = which ? pooled_k : pooled_q;
+      dst[(bh * g.max_tiles + i) * D + tid] = (float)(s / (double)t.nvalid);
+    }
+    __syncthreads();
+  }
+}
+
+// Tile-major rows back to raster order (valid slots only).
+template <int D>
+__global__ __launch_bounds__(kLayoutThreads) void untile_kernel(Geo g, const uint16_t* __restrict__ xt,
+                                                               const int* __restrict__ cand,
+                                                               uint16_t* __restrict__ out) {
+  constexpr int P = D / 8;
+  const int i = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int c = cand ? cand[bh] : 0;
+  const BlkGeo b = pick_blk(g, c);
+  if (i >= b.n_tiles) return;
+  const TileRef t = tile_ref(g, b, i);
+  const long tm_base = bh * g.tok_cap * D + (long)i * b.slots * D;
+  for (int e = threadIdx.x; e < t.nvalid * P; e += kLayoutThreads) {
+    const int s = e / P, p = e % P;
+    const uint4 val = *reinterpret_cast<const uint4*>(xt + tm_base + (long)s * D + p * 8);
+    *reinterpret_cast<uint4*>(out + bh * (long)g.N * D + token_of(g, b, t, s) * D + p * 8) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection: one workgroup per (head, query tile).
+
+constexpr int kSelThreads = 256;
+constexpr int kMaxTiles = 4096;
+
+__device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float* __restrict__ pooled_q,
+                                                             const float* __restrict__ pooled_k,
+                                                             const int* __restrict__ cand,
+                                                             int* __restrict__ row_len,
+                                                             int* __restrict__ col_idx) {
+  __shared__ unsigned char keep[kMaxTiles];
+  __shared__ double sc[kMaxTiles];
+  __shared__ int sid[kMaxTiles];
+  __shared__ float qbar[128];
+  __shared__ int cnt[kSelThreads];
+
+  const int i = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int c = cand ? cand[bh] : 0;
+  const BlkGeo b = pick_blk(g, c);
+  const int n = b.n_tiles;
+  if (i >= n) return;
+  const int tid = threadIdx.x;
+  const int D = g.d;
+  const bool dense = (g.flags & VSA_DENSE) != 0;
+  for (int j = tid; j < n; j += kSelThreads) keep[j] = dense ? 1 : 0;
+  __syncthreads();
+
+  if (g.flags & VSA_WINDOW) {
+    const int ci[3] = {i / (b.nt[1] * b.nt[2]), (i / b.nt[2]) % b.nt[1], i % b.nt[2]};
+    int lo[3], hi[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const int r = (g.win[a] - 1) / 2;
+      const int nn = b.nt[a];
+      if (g.win_mode == VSA_WIN_CLAMP && nn >= 2 * r + 1) {
+        lo[a] = min(max(ci[a] - r, 0), nn - (2 * r + 1));
+        hi[a] = lo[a] + 2 * r;
+      } else {
+        lo[a] = max(ci[a] - r, 0);
+        hi[a] = min(ci[a] + r, nn - 1);
+      }
+    }
+    const int e1 = hi[1] - lo[1] + 1, e2 = hi[2] - lo[2] + 1;
+    const int cells = (hi[0] - lo[0] + 1) * e1 * e2;
+    for (int x = tid; x < cells; x += kSelThreads) {
+      const int a0 = lo[0] + x / (e1 * e2);
+      const int a1 = lo[1] + (x / e2) % e1;
+      const int a2 = lo[2] + x % e2;
+      keep[(a0 * b.nt[1] + a1) * b.nt[2] + a2] = 1;
+    }
+  }
+
+  const bool topp = (g.flags & VSA_TOPP) != 0;
+  const int K = b.topk;
+  if (topp || K > 0) {
+    for (int x = tid; x < D; x += kSelThreads) qbar[x] = pooled_q[(bh * g.max_tiles + i) * D + x];
+    __syncthreads();
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int j = tid; j < m; j += kSelThreads) {
+      if (j < n) {
+        const float* kr = pooled_k + (bh * g.max_tiles + j) * D;
+        double acc = 0.0;
+        // Fixed left-to-right order; each fp32 x fp32 product is exact in
+        // fp64, so a fused multiply-add rounds exactly like mul-then-add.
+        for (int x = 0; x < D; ++x) acc = fma((double)qbar[x], (double)kr[x], acc);
+        sc[j] = acc * g.scale;
+        sid[j] = j;
+      } else {
+        sc[j] = -DBL_MAX;
+        sid[j] = INT_MAX;
+      }
+    }
+    __syncthreads();
+    // Bitonic sort: highest score first, ties by lower tile index.
+    for (int kk = 2; kk <= m; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int x = tid; x < m; x += kSelThreads) {
+          const int y = x ^ jj;
+          if (y > x) {
+            const bool up = (x & kk) == 0;
+            const bool yfirst = ranks_before(sc[y], sid[y], sc[x], sid[x]);
+            if (yfirst == up) {
+              const double ts = sc[x];
+              sc[x] = sc[y];
+              sc[y] = ts;
+              const int ti = sid[x];
+              sid[x] = sid[y];
+              sid[y] = ti;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int r = tid; r < K; r += kSelThreads) keep[sid[r]] = 1;
+    if (topp && tid == 0) {
+      const double mx = sc[0];
+      double z = 0.0;
+      for (int r = 0; r < n; ++r) z += exp(sc[r] - mx);
+      double cum = 0.0;
+      for (int r = 0; r < n; ++r) {
+        keep[sid[r]] = 1;
+        cum += exp(sc[r] - mx) / z;
+        if (cum >= g.topp) break;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Ascending compaction of the kept flags.
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int j0 = tid * per;
+  const int j1 = min(n, j0 + per);
+  int local = 0;
+  for (int j = j0; j < j1; ++j) local += keep[j];
+  cnt[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int x = 0; x < kSelThreads; ++x) {
+      const int v = cnt[x];
+      cnt[x] = run;
+      run += v;
+    }
+    row_len[bh * g.max_tiles + i] = min(run, g.row_cap);
+  }
+  __syncthreads();
+  int pos = cnt[tid];
+  int* dst = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
+  for (int j = j0; j < j1; ++j)
+    if (keep[j]) {
+      if (pos < g.row_cap) dst[pos] = j;
+      ++pos;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, bool pool, hipStream_t s) {
+  dim3 grid(g.max_tiles, g.B * g.H);
+  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  if (g.d == 128)
+    hipLaunchKernelGGL(layout_kernel<128>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
+                       w.vt, w.pooled_q, w.pooled_k, cand, pool ? 1 : 0);
+  else
+    hipLaunchKernelGGL(layout_kernel<64>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
+                       w.vt, w.pooled_q, w.pooled_k, cand, pool ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s) {
+  dim3 grid(g.max_tiles, g.B * g.H);
+  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  const uint16_t* src = which ? w.kt : w.qt;
+  if (g.d == 128)
+    hipLaunchKernelGGL(untile_kernel<128>, grid, dim3(kLayoutThreads), 0, s, g, src, cand, out);
+  else
+    hipLaunchKernelGGL(untile_kernel<64>, grid, dim3(kLayoutThreads), 0, s, g, src, cand, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
+  dim3 grid(g.max_tiles, g.B * g.H);
+  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, g, w.pooled_q, w.pooled_k, cand,
+                     w.row_len, w.col_idx);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,94 @@
+// Internal definitions shared by the host API and the HIP kernels of libvsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vsa.h"
+
+namespace vsa {
+
+// One blocking of the token grid (tile extents and derived counts).
+struct BlkGeo {
+  int tile[3];   // tokens per tile along t, h, w
+  int nt[3];     // tiles along t, h, w
+  int n_tiles;   // nt[0]*nt[1]*nt[2]
+  int slots;     // tokens per tile rounded up to a multiple of 32
+  int topk;      // resolved K for this blocking (0 = off)
+};
+
+// Everything a kernel needs to know about the problem; passed by value.
+struct Geo {
+  int B, H, d, N;
+  int grid[3];
+  int nb;           // number of blockings (1, or the SICS candidates)
+  BlkGeo blk[VSA_MAX_CAND];
+  int max_tiles;
+  long tok_cap;     // max over blockings of n_tiles*slots (tile-major rows per head)
+  int row_cap;      // capacity of one kept-tile row
+  uint32_t flags;
+  int win[3];
+  int win_mode;
+  double topp;
+  double scale;     // softmax scale
+  // fine-grained mask
+  int fine_M, fine_G;
+  long fine_keep;   // kept (group, key) pairs per head (target count)
+  long fine_cap;    // kept-key list capacity per head
+  // SICS atoms: common refinement of the candidate blockings
+  int atom[3];
+  int na[3];
+  int n_atoms;
+};
+
+// Blocking c of g, field by field with selects: indexing the by-value kernel
+// argument with a runtime c would place the whole array in scratch memory.
+__host__ __device__ __forceinline__ int sel4(int c, int a0, int a1, int a2, int a3) {
+  return c == 0 ? a0 : (c == 1 ? a1 : (c == 2 ? a2 : a3));
+}
+__host__ __device__ __forceinline__ BlkGeo pick_blk(const Geo& g, int c) {
+  BlkGeo b;
+#define VSA_PICK(f) b.f = sel4(c, g.blk[0].f, g.blk[1].f, g.blk[2].f, g.blk[3].f)
+  VSA_PICK(tile[0]); VSA_PICK(tile[1]); VSA_PICK(tile[2]);
+  VSA_PICK(nt[0]); VSA_PICK(nt[1]); VSA_PICK(nt[2]);
+  VSA_PICK(n_tiles); VSA_PICK(slots); VSA_PICK(topk);
+#undef VSA_PICK
+  return b;
+}
+
+// Workspace pointers resolved from the plan's layout.
+struct Ws {
+  uint16_t* qt;
+  uint16_t* kt;
+  uint16_t* vt;
+  float* pooled_q;
+  float* pooled_k;
+  int* row_len;
+  int* col_idx;
+  int* cand;
+  float* cand_score;
+  float* tile_sics;
+  float* atoms;
+  float* fine_qbar;
+  double* fine_tau;
+  int* fine_count;
+  int* fine_idx;
+  int* fine_ptr;
+  unsigned char* scratch;
+};
+
+// Kernel launchers (kernels.hip / sics.hip / fine.hip); return hipError_t.
+hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, bool pool, hipStream_t s);
+hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s);
+hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s);
+hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s);
+hipError_t launch_sics(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                       hipStream_t s);
+hipError_t launch_fine_select(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                              hipStream_t s);
+hipError_t launch_fine_attend(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, uint16_t* o, hipStream_t s);
+
+}  // namespace vsa

@@ -1,0 +1,221 @@
+/*
+ * vsa.h - block-sparse self-attention over a 3D video token grid (MI355X).
+ *
+ * C ABI of libvsa.so.  Plain pointers and sizes only.  Device pointers are
+ * HIP device memory owned by the caller; `stream` is a hipStream_t passed
+ * as void* (NULL = the default stream).  Every call returns a status code
+ * (VSA_OK = 0); no C++ exception crosses this boundary.  A failing call
+ * leaves a message readable with vsa_last_error() on the calling thread.
+ *
+ * What is computed (sources are public web pages, cited by page/section):
+ *   - the token grid T x H x W is cut into 3D tiles; one tile is one
+ *     attention block and tokens inside a tile stay consecutive
+ *     (Sliding Tile Attention verdict page, arXiv 2502.04507,
+ *     pith_extraction.key_machinery);
+ *   - each head may pick, among candidate blockings, the one whose tiles
+ *     are most self-similar by SICS, the sum of intra-block cosine
+ *     similarities (SPADE review page, arXiv 2608.03335, "Core claim",
+ *     "What carries the argument", Figure 3);
+ *   - each query tile keeps a set of key tiles: a sliding tile window
+ *     (STA page, pith_extraction.pith_summary) and/or a Top-K / Top-P filter
+ *     on pooled-mean block scores (SPADE page, "Core claim"; Figure 4);
+ *   - alternatively a fine-grained mask keeps individual keys for groups of
+ *     M consecutive queries, by thresholding k . mean(q_group)
+ *     (FG-Attn verdict page, arXiv 2509.16518, pith_extraction.key_machinery,
+ *     referee_report.major_comments[1]);
+ *   - attention is then softmax(scale * q k^T) v restricted to the kept
+ *     keys, computed with an online softmax (SPADE page, ledger axiom on
+ *     FlashAttention-style online softmax).
+ *
+ * Tensor layout.  q, k, v, o are contiguous bf16 [B, H, N, d] with
+ * N = T*H*W tokens in raster order (t, h, w), w fastest; 16-byte aligned.
+ * d must be 64 or 128.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define VSA_OK                      0
+#define VSA_ERR_INVALID_ARG         1  /* null pointer, bad size/shape/policy */
+#define VSA_ERR_UNSUPPORTED         2  /* valid but outside what is built */
+#define VSA_ERR_WORKSPACE_TOO_SMALL 3
+#define VSA_ERR_HIP                 4  /* a HIP runtime call failed (text in vsa_last_error) */
+
+/* ---- dtypes ------------------------------------------------------------ */
+#define VSA_BF16 1
+
+/* ---- mask policy flags (combine with |) --------------------------------
+ * VSA_DENSE       every key tile (all-ones block mask).
+ * VSA_WINDOW      sliding tile window of win[] tiles (odd full extents).
+ * VSA_TOPK        the `topk` highest-scoring key tiles per query tile.
+ * VSA_TOPK_FRAC   Top-K with K = ceil(topk_frac * n_tiles) (per blocking).
+ * VSA_TOPP        smallest set of highest-scoring key tiles whose softmax
+ *                 mass over the row reaches `topp`.
+ * VSA_SICS_SELECT per head, pick among problem.cand_tile[] by SICS.
+ * VSA_FINE        fine-grained M x 1 mask (M = fine_group), keep fraction
+ *                 fine_keep of all (group, key) pairs per head.  Exclusive
+ *                 with every other flag.
+ * Window, Top-K and Top-P combine as a union.  Top-K over all key tiles,
+ * then union with the window.                                             */
+#define VSA_DENSE        0x01u
+#define VSA_WINDOW       0x02u
+#define VSA_TOPK         0x04u
+#define VSA_TOPK_FRAC    0x08u
+#define VSA_TOPP         0x10u
+#define VSA_SICS_SELECT  0x20u
+#define VSA_FINE         0x40u
+
+#define VSA_WIN_TRUNCATE 0  /* window cut at the grid edge */
+#define VSA_WIN_CLAMP    1  /* window shifted inward, keeps its full size */
+
+#define VSA_MAX_CAND 4
+
+typedef struct vsa_problem {
+  int32_t B, H, d;
+  int32_t grid[3];                    /* T, H, W in tokens */
+  int32_t tile[3];                    /* tile extents (t, h, w) when SICS is off */
+  int32_t n_cand;                     /* candidate blockings for SICS (<= 4) */
+  int32_t cand_tile[VSA_MAX_CAND][3];
+  int32_t dtype;                      /* VSA_BF16 */
+} vsa_problem;
+
+typedef struct vsa_mask_policy {
+  uint32_t flags;
+  int32_t win[3];         /* window extent in tiles per axis, odd, >= 1 */
+  int32_t win_mode;       /* VSA_WIN_TRUNCATE or VSA_WIN_CLAMP */
+  int32_t topk;           /* for VSA_TOPK */
+  double topk_frac;       /* for VSA_TOPK_FRAC, in (0, 1] */
+  double topp;            /* for VSA_TOPP, in (0, 1] */
+  int32_t fine_group;     /* M for VSA_FINE, multiple of 16, >= 16 */
+  double fine_keep;       /* kept fraction for VSA_FINE, in (0, 1] */
+  double scale;           /* softmax scale; 0 selects 1/sqrt(d) */
+} vsa_mask_policy;
+
+/* Opaque, immutable plan; safe to share between threads. */
+typedef struct vsa_plan_s vsa_plan_t;
+
+/* Facts about a plan (host data). */
+typedef struct vsa_plan_info {
+  int32_t n_blockings;            /* 1, or n_cand under VSA_SICS_SELECT */
+  int32_t ntiles[VSA_MAX_CAND][3];/* tiles per axis of each blocking */
+  int32_t n_tiles[VSA_MAX_CAND];  /* tiles of each blocking */
+  int32_t slots[VSA_MAX_CAND];    /* tokens per tile rounded up to 32 */
+  int32_t topk[VSA_MAX_CAND];     /* resolved K per blocking (0 = off) */
+  int32_t max_tiles;              /* max n_tiles over blockings */
+  int32_t row_cap;                /* capacity of one kept-tile row */
+  int64_t static_pairs;           /* kept tile pairs per head if the mask is
+                                     input-independent, else -1 */
+  double static_flops;            /* 4 d sum n_i n_j over static pairs, all
+                                     heads and batches; 0 if dynamic */
+  int32_t fine_groups;            /* G for VSA_FINE, else 0 */
+  int64_t fine_keep_count;        /* kept (group, key) pairs per head target */
+  int64_t fine_cap;               /* capacity of the kept-key list per head */
+  double scale;                   /* resolved softmax scale */
+} vsa_plan_info;
+
+/* Workspace regions, for inspection by tests (see vsa_workspace_region). */
+#define VSA_WS_QT          0  /* bf16 [B*H][tiles*slots][d] tile-major Q */
+#define VSA_WS_KT          1  /* bf16 [B*H][tiles*slots][d] tile-major K */
+#define VSA_WS_VT          2  /* bf16 [B*H][tiles][d][slots] tile-major V, transposed per tile */
+#define VSA_WS_POOLED_Q    3  /* fp32 [B*H][max_tiles][d] */
+#define VSA_WS_POOLED_K    4  /* fp32 [B*H][max_tiles][d] */
+#define VSA_WS_ROW_LEN     5  /* int32 [B*H][max_tiles] kept tiles per row */
+#define VSA_WS_COL_IDX     6  /* int32 [B*H][max_tiles][row_cap] ascending */
+#define VSA_WS_CAND        7  /* int32 [B*H] chosen blocking */
+#define VSA_WS_CAND_SCORE  8  /* fp32 [B*H][n_blockings] mean pair cosine */
+#define VSA_WS_TILE_SICS   9  /* fp32 [B*H][n_blockings][2][max_tiles] SICS of Q, K */
+#define VSA_WS_ATOMS      10  /* fp32 SICS partial sums of unit vectors */
+#define VSA_WS_FINE_QBAR  11  /* fp32 [B*H][G][d] group means of Q */
+#define VSA_WS_FINE_TAU   12  /* fp64 [B*H] per-head score threshold */
+#define VSA_WS_FINE_COUNT 13  /* int32 [B*H][G] kept keys per group */
+#define VSA_WS_FINE_IDX   14  /* int32 [B*H][fine_cap] kept keys, groups in order */
+#define VSA_WS_FINE_PTR   15  /* int32 [B*H][G+1] start of each group's keys */
+#define VSA_WS_SCRATCH    16  /* internal */
+#define VSA_WS_NREGIONS   17
+
+/* ---- plan ---------------------------------------------------------------
+ * Validates `prob` and `pol`, computes the tile geometry of every blocking,
+ * the static window statistics and the workspace layout.  Host only: makes
+ * no HIP call and needs no GPU.  On success *out owns a plan that the caller
+ * releases with vsa_plan_destroy.  Errors: VSA_ERR_INVALID_ARG for null
+ * pointers, non-positive sizes, even/zero window extents, fractions outside
+ * (0,1], conflicting flags; VSA_ERR_UNSUPPORTED for d not in {64,128},
+ * dtype other than bf16, more than 4096 tiles, or a tile larger than the
+ * grid. */
+int vsa_plan(const vsa_problem* prob, const vsa_mask_policy* pol, vsa_plan_t** out);
+void vsa_plan_destroy(vsa_plan_t* plan);
+int vsa_plan_get_info(const vsa_plan_t* plan, vsa_plan_info* info);
+
+/* Workspace bytes the caller must provide to the calls below (host only). */
+int vsa_workspace_bytes(const vsa_plan_t* plan, size_t* bytes);
+/* Byte offset and size of one VSA_WS_* region inside the workspace. */
+int vsa_workspace_region(const vsa_plan_t* plan, int region, size_t* offset, size_t* bytes);
+
+/* ---- execution ----------------------------------------------------------
+ * All of these enqueue kernels on `stream` and return without waiting; they
+ * allocate nothing and never synchronize.  Argument errors are reported
+ * before anything is enqueued; a HIP launch error returns VSA_ERR_HIP.
+ * Kernel faults surface at the caller's next synchronization.  The
+ * workspace (>= vsa_workspace_bytes, 256-byte aligned) is owned by the
+ * caller and must not be shared by calls that overlap in time.
+ *
+ * vsa_forward = vsa_layout + vsa_select + vsa_attend.  o receives the
+ * attention output in the same raster layout as q. */
+int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage 1, layout: under VSA_SICS_SELECT scores every candidate blocking by
+ * SICS and records the chosen one per head; then copies Q, K (tile-major)
+ * and V (tile-major, transposed per tile) into the workspace, padding each
+ * tile with zeros up to its slot count, and, for dynamic masks, writes the
+ * per-tile mean of Q and K.  Nothing to do under VSA_FINE. */
+int vsa_layout(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage 2, selection: the kept key tiles of every query tile (ascending,
+ * in the workspace's ROW_LEN / COL_IDX regions), or under VSA_FINE the kept
+ * keys of every query group.  Reads q, k only under VSA_FINE. */
+int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage 3, attention: block-sparse (or fine-grained) attention with online
+ * softmax, fp32 accumulation, bf16 output written straight to raster `o`.
+ * Requires stages 1 and 2 on the same workspace. */
+int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+               void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/* Inverse layout: copy the workspace's tile-major Q (which = 0) or K
+ * (which = 1) back to raster bf16 [B, H, N, d] in `out`, dropping pads. */
+int vsa_untile(const vsa_plan_t* plan, int which, const void* workspace, size_t ws_bytes,
+               void* out, void* stream);
+
+/* ---- debug getters (synchronize `stream`) -------------------------------
+ * Copies the tile selection to host memory as CSR over rows r = (b*H + h) *
+ * max_tiles + i: row_ptr has B*H*max_tiles + 1 entries, col_idx capacity
+ * col_cap entries (B*H*max_tiles*row_cap always suffices); *n_kept receives
+ * the number of entries written.  cand (may be NULL) receives B*H chosen
+ * blockings.  Returns VSA_ERR_WORKSPACE_TOO_SMALL when col_cap is short. */
+int vsa_read_selection(const vsa_plan_t* plan, const void* workspace, size_t ws_bytes,
+                       int32_t* row_ptr, int32_t* col_idx, size_t col_cap,
+                       int64_t* n_kept, int32_t* cand, void* stream);
+
+/* Retained work of the current selection: kept tile pairs (or fine
+ * (group, key) pairs) summed over heads, and 4*d*sum(n_query*n_key) FLOPs
+ * over valid tokens.  Synchronizes `stream`. */
+int vsa_retained_work(const vsa_plan_t* plan, const void* workspace, size_t ws_bytes,
+                      int64_t* pairs, double* flops, void* stream);
+
+const char* vsa_status_string(int status);
+const char* vsa_last_error(void);   /* thread-local, "" if none */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H */

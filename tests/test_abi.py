@@ -1,0 +1,163 @@
+"""C-ABI checks that need no GPU: exports, plan validation, geometry facts."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_tile_amd as vsa
+from block_sparse_attention_tile_amd import _lib
+from oracle import geometry
+from synth import CONFIGS
+from tests.helpers import structs_of
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "vsa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(_lib.EXPORTED) == declared
+
+
+def test_status_strings():
+    L = vsa.lib()
+    assert L.vsa_status_string(0) == b"VSA_OK"
+    assert L.vsa_status_string(3) == b"VSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan480", "hunyuan", "wan14b", "fine"])
+def test_plan_for_every_workload(name):
+    wl = CONFIGS[name]
+    prob, pol = structs_of(wl)
+    h = vsa.vsa_plan(prob, pol)
+    info = vsa.vsa_plan_get_info(h)
+    assert vsa.vsa_workspace_bytes(h) > 0
+    if wl.fine_group:
+        assert info.fine_groups == 512
+        assert info.fine_keep_count == 2515968
+    else:
+        tiles = wl.candidates or (wl.tile,)
+        for c, t in enumerate(tiles):
+            nt = geometry.tile_counts(wl.grid, t)
+            assert tuple(info.ntiles[c]) == nt
+            bs = t[0] * t[1] * t[2]
+            assert info.slots[c] == -(-bs // 32) * 32
+    vsa.vsa_plan_destroy(h)
+
+
+def _static_flops(wl, mode):
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    nt = geometry.tile_counts(wl.grid, wl.tile)
+    tot = 0.0
+    pairs = 0
+    for i in range(len(mem)):
+        for j in geometry.window(i, nt, wl.window, mode):
+            tot += len(mem[i]) * len(mem[j])
+            pairs += 1
+    return pairs, tot * 4 * wl.d * wl.B * wl.H
+
+
+@pytest.mark.parametrize("mode,code", [("truncate", vsa.VSA_WIN_TRUNCATE), ("clamp", vsa.VSA_WIN_CLAMP)])
+def test_static_window_work_matches_oracle(mode, code):
+    wl = CONFIGS["hunyuan"]
+    prob, _ = structs_of(wl)
+    pol = vsa.make_policy(vsa.VSA_WINDOW, win=wl.window, win_mode=code)
+    info = vsa.vsa_plan_get_info(vsa.vsa_plan(prob, pol))
+    pairs, fl = _static_flops(wl, mode)
+    assert info.static_pairs == pairs
+    assert info.static_flops == pytest.approx(fl, rel=1e-12)
+    assert info.row_cap == 45
+
+
+def test_ragged_static_flops():
+    wl = CONFIGS["wan480"].with_(topp=0.0)
+    prob, pol = structs_of(wl)
+    info = vsa.vsa_plan_get_info(vsa.vsa_plan(prob, pol))
+    pairs, fl = _static_flops(wl, "truncate")
+    assert info.static_pairs == pairs == 4693
+    assert info.static_flops == pytest.approx(fl, rel=1e-12)
+
+
+def _err(prob, pol):
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_plan(prob, pol)
+    return e.value.status
+
+
+def test_plan_errors():
+    ok = vsa.make_problem(1, 2, 64, (4, 8, 8), (2, 4, 4))
+    win = vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3))
+    assert _err(vsa.make_problem(1, 2, 96, (4, 8, 8), (2, 4, 4)), win) == vsa._lib.VSA_ERR_UNSUPPORTED
+    assert _err(vsa.make_problem(0, 2, 64, (4, 8, 8), (2, 4, 4)), win) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(vsa.make_problem(1, 2, 64, (4, 8, 8), (8, 4, 4)), win) == vsa._lib.VSA_ERR_UNSUPPORTED
+    assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(2, 3, 3))) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(0)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_TOPP, topp=1.5)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_TOPK)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_TOPK | vsa.VSA_TOPK_FRAC, topk=2, topk_frac=0.5)) \
+        == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_FINE | vsa.VSA_WINDOW, win=(3, 3, 3), fine_group=64,
+                                    fine_keep=0.1)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_FINE, fine_group=40, fine_keep=0.1)) \
+        == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_SICS_SELECT | vsa.VSA_TOPK, topk=2)) \
+        == vsa._lib.VSA_ERR_INVALID_ARG          # n_cand = 0
+    assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), scale=-1.0)) \
+        == vsa._lib.VSA_ERR_INVALID_ARG
+    with pytest.raises(vsa.VsaError):
+        vsa.vsa_plan(None, win) if False else _lib._check(vsa.lib().vsa_plan(None, None, None))
+
+
+def test_exec_argument_errors_before_any_device_call():
+    prob = vsa.make_problem(1, 2, 64, (4, 8, 8), (2, 4, 4))
+    h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3)))
+    n = vsa.vsa_workspace_bytes(h)
+    L = vsa.lib()
+    buf = ctypes.create_string_buffer(n + 512)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    assert L.vsa_forward(h, None, 16, 16, 16, base, n, None) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_forward(h, 16, 16, 16, 16, base, n - 1, None) == vsa._lib.VSA_ERR_WORKSPACE_TOO_SMALL
+    assert L.vsa_forward(h, 16, 16, 16, 16, base + 16, n, None) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert L.vsa_forward(h, 17, 16, 16, 16, base, n, None) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert b"workspace" in L.vsa_last_error() or b"aligned" in L.vsa_last_error()
+
+
+def test_forward_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    prob = vsa.make_problem(1, 2, 64, (4, 8, 8), (2, 4, 4))
+    h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3)))
+    n = vsa.vsa_workspace_bytes(h)
+    buf = ctypes.create_string_buffer(n + 512)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    st = vsa.lib().vsa_forward(h, 16, 16, 16, 16, base, n, None)
+    assert st == vsa._lib.VSA_ERR_HIP
+
+
+def test_workspace_regions_disjoint_and_aligned():
+    wl = CONFIGS["wan14b"]
+    prob, pol = structs_of(wl)
+    h = vsa.vsa_plan(prob, pol)
+    total = vsa.vsa_workspace_bytes(h)
+    spans = []
+    for r in range(_lib.VSA_WS_NREGIONS):
+        off, n = vsa.vsa_workspace_region(h, r)
+        if n:
+            assert off % 256 == 0
+            assert off + n <= total
+            spans.append((off, off + n))
+    spans.sort()
+    for a, b in zip(spans, spans[1:]):
+        assert a[1] <= b[0]

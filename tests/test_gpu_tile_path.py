@@ -1,0 +1,161 @@
+"""GPU parity of the tile path (layout, selection, attention) against the oracle.
+
+Every case prints its name before touching the GPU so a failing run names it.
+Tolerances: tile indices bit-exact; pooled means bit-exact (exact sums,
+one rounding); attention output max-abs <= 2e-2 (bf16 I/O, fp32 accumulate).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as vsa
+from block_sparse_attention_tile_amd import _lib
+from oracle import attention, geometry, layout, select
+from synth import CONFIGS, Workload, smooth_field_qkv
+from tests.helpers import csr_rows, oracle_tile_rows, structs_of
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-2
+
+SMALL = {
+    # dense 8-tile problem, 32-token tiles, d=64
+    "tiny": CONFIGS["tiny"],
+    # ragged edge tiles (grid not divisible), 24-token tiles -> 32 slots
+    "ragged_d64": Workload("ragged_d64", 1, 3, 64, (5, 7, 9), (2, 3, 4), window=(3, 3, 3), topk=3),
+    # Wan-480p tile shape (144 tokens -> 160 slots, a 32-key tail chunk),
+    # partial last W tile, Top-P + window
+    "w480_mini": Workload("w480_mini", 1, 2, 128, (6, 12, 20), (3, 6, 8), window=(3, 3, 3), topp=0.9),
+    # HunyuanVideo tile shape (384 tokens), static window 3x3x5, d=128
+    "hy_mini": Workload("hy_mini", 1, 2, 128, (12, 16, 24), (6, 8, 8), window=(3, 3, 5)),
+    # clamp-mode window
+    "hy_mini_clamp": Workload("hy_mini_clamp", 1, 1, 128, (12, 16, 40), (6, 8, 8), window=(1, 1, 3),
+                              win_mode="clamp"),
+    # dense, two batches
+    "dense_b2": Workload("dense_b2", 2, 2, 64, (3, 5, 6), (1, 5, 6)),
+    # Top-K only (scores decide everything), d=128, 112-token tiles
+    "topk_only": Workload("topk_only", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3),
+}
+
+
+def _say(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def _inputs(wl, device="cuda", seed=0):
+    return smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=seed, device=device)
+
+
+def _run_all(wl, q, k, v):
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    o = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    return plan, o
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layout_roundtrip_and_tile_major(name):
+    wl = SMALL[name]
+    _say(f"layout {name}")
+    q, k, v = _inputs(wl)
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    plan.layout(q, k, v)
+    back_q = plan.untile(0, torch.zeros_like(q))
+    back_k = plan.untile(1, torch.zeros_like(k))
+    torch.cuda.synchronize()
+    assert torch.equal(back_q, q) and torch.equal(back_k, k)
+    slots = plan.info.slots[0]
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    nT = len(mem)
+    want_q = layout.to_tile_major(q.view(torch.int16).cpu().numpy(), mem, slots)
+    got_q = plan.region(_lib.VSA_WS_QT, torch.int16).view(wl.B, wl.H, nT, slots, wl.d).cpu().numpy()
+    assert np.array_equal(got_q, want_q)
+    want_v = layout.to_tile_major(v.view(torch.int16).cpu().numpy(), mem, slots)
+    got_vt = plan.region(_lib.VSA_WS_VT, torch.int16).view(wl.B, wl.H, nT, wl.d, slots).cpu().numpy()
+    assert np.array_equal(got_vt.transpose(0, 1, 2, 4, 3), want_v)
+
+
+@pytest.mark.parametrize("name", [n for n, w in SMALL.items() if w.topk or w.topp])
+def test_pooled_means_bit_exact(name):
+    wl = SMALL[name]
+    _say(f"pooled {name}")
+    q, k, v = _inputs(wl)
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    plan.layout(q, k, v)
+    torch.cuda.synchronize()
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    nT = len(mem)
+    pq = plan.region(_lib.VSA_WS_POOLED_Q, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
+    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
+    qn, kn = q.float().cpu().numpy(), k.float().cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            assert np.array_equal(pq[b * wl.H + h], select.pooled_means(qn[b, h], mem))
+            assert np.array_equal(pk[b * wl.H + h], select.pooled_means(kn[b, h], mem))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_selection_and_attention_small(name):
+    wl = SMALL[name]
+    _say(f"forward {name}")
+    q, k, v = _inputs(wl)
+    plan, o = _run_all(wl, q, k, v)
+    row_ptr, col, _ = plan.read_selection()
+    qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
+    on = o.float().cpu().numpy()
+    nT = plan.info.n_tiles[0]
+    for b in range(wl.B):
+        for h in range(wl.H):
+            bh = b * wl.H + h
+            rows, margins, mem = oracle_tile_rows(wl, qn[b, h], kn[b, h], wl.tile)
+            got = csr_rows(row_ptr, col, bh, plan.info.max_tiles, nT)
+            for i in range(nT):
+                if margins[i] > 1e-9:
+                    assert got[i] == rows[i], (b, h, i)
+            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, got)
+            err = np.abs(on[b, h] - ref).max()
+            assert err <= ATOL, (b, h, err)
+
+
+def test_forward_is_deterministic_and_stage_split_matches():
+    wl = SMALL["w480_mini"]
+    _say("determinism w480_mini")
+    q, k, v = _inputs(wl, seed=5)
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    o1 = plan.forward(q, k, v)
+    ws = plan.workspace()
+    ws.fill_(0xFF)                      # poison: NaN patterns everywhere
+    o2 = plan.forward(q, k, v)
+    o3 = torch.empty_like(q)
+    plan.layout(q, k, v)
+    plan.select()
+    plan.attend(o3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_hunyuan_full_size_sampled():
+    """HunyuanVideo 720p shape: all heads' selection, sampled query tiles of O."""
+    wl = CONFIGS["hunyuan"]
+    _say("hunyuan full size")
+    q, k, v = _inputs(wl)
+    plan, o = _run_all(wl, q, k, v)
+    row_ptr, col, _ = plan.read_selection()
+    nT = plan.info.n_tiles[0]
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    nt = geometry.tile_counts(wl.grid, wl.tile)
+    want = [geometry.window(i, nt, wl.window) for i in range(nT)]
+    for bh in range(wl.B * wl.H):
+        assert csr_rows(row_ptr, col, bh, plan.info.max_tiles, nT) == want
+    rng = np.random.default_rng(0)
+    for h in (0, 13, 23):
+        qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
+        on = o[0, h].float().cpu().numpy()
+        tiles = sorted(set(rng.choice(nT, 6, replace=False).tolist()) | {0, nT - 1, 155})
+        ref = attention.block_sparse_attention(qn, kn, vn, mem, want, query_tiles=tiles)
+        for i in tiles:
+            err = np.abs(on[mem[i]] - ref[mem[i]]).max()
+            assert err <= ATOL, (h, i, err)
