@@ -65,24 +65,28 @@ def _cpu_baseline(wl, q, k, v, plan, budget_s):
     mt = plan.info.max_tiles
     nT = plan.info.n_tiles[0]
     mem = geometry.tile_members(wl.grid, wl.tile)
-    h = 0
-    rows = [col[row_ptr[h * mt + i]:row_ptr[h * mt + i + 1]].tolist() for i in range(nT)]
-    qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
-    order = np.random.default_rng(0).permutation(nT)
-    done, flops = [], 0.0
+    done, flops = 0, 0.0
     t0 = time.perf_counter()
-    for i in order:
-        attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=[int(i)])
-        done.append(int(i))
-        flops += 4.0 * wl.d * len(mem[i]) * sum(len(mem[j]) for j in rows[i])
+    heads = 0
+    for h in range(wl.B * wl.H):
+        b_, hh = divmod(h, wl.H)
+        rows = [col[row_ptr[h * mt + i]:row_ptr[h * mt + i + 1]].tolist() for i in range(nT)]
+        qn, kn, vn = (t[b_, hh].float().cpu().numpy() for t in (q, k, v))
+        for i in np.random.default_rng(h).permutation(nT):
+            attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=[int(i)])
+            done += 1
+            flops += 4.0 * wl.d * len(mem[i]) * sum(len(mem[j]) for j in rows[i])
+            if time.perf_counter() - t0 > budget_s:
+                break
+        heads += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"head 0, {len(done)} of {nT} query tiles ({len(done) * len(mem[0])} "
-                      f"query rows), fp64 numpy masked-softmax attention; "
-                      f"{dt:.1f} s; {flops:.3e} retained FLOPs",
+            "sample": f"{done} query tiles of {nT} per head over {heads} head(s) "
+                      f"({done * len(mem[0])} query rows), fp64 numpy masked-softmax "
+                      f"attention; {dt:.1f} s; {flops:.3e} retained FLOPs",
             "ms_per_call_extrapolated": dt / flops * plan_total_flops(plan) * 1e3}
 
 
@@ -109,7 +113,7 @@ def main():
     import torch
     import block_sparse_attention_tile_amd as vsa
     from synth import CONFIGS, smooth_field_qkv
-    from tests.helpers import structs_of
+    from block_sparse_attention_tile_amd.workload import plan_structs as structs_of
 
     wl = CONFIGS[args.config]
     dev = torch.device("cuda:0")

@@ -16,6 +16,9 @@ from ._lib import (  # noqa: F401
 )
 
 
+from .workload import flags_of, plan_structs  # noqa: E402,F401
+
+
 def _ptr(t):
     return t.data_ptr() if t is not None else None
 

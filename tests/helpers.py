@@ -7,32 +7,7 @@ import block_sparse_attention_tile_amd as vsa
 from oracle import attention, fine, geometry, select, sics
 
 
-def flags_of(wl):
-    f = 0
-    if wl.fine_group:
-        return vsa.VSA_FINE
-    if wl.window is not None:
-        f |= vsa.VSA_WINDOW
-    if wl.topk:
-        f |= vsa.VSA_TOPK
-    if wl.topk_frac:
-        f |= vsa.VSA_TOPK_FRAC
-    if wl.topp:
-        f |= vsa.VSA_TOPP
-    if wl.candidates:
-        f |= vsa.VSA_SICS_SELECT
-    if f == 0:
-        f = vsa.VSA_DENSE
-    return f
-
-
-def structs_of(wl):
-    prob = vsa.make_problem(wl.B, wl.H, wl.d, wl.grid, wl.tile, wl.candidates)
-    pol = vsa.make_policy(flags_of(wl), win=wl.window or (1, 1, 1),
-                          win_mode=vsa.VSA_WIN_CLAMP if wl.win_mode == "clamp" else vsa.VSA_WIN_TRUNCATE,
-                          topk=wl.topk, topk_frac=wl.topk_frac, topp=wl.topp,
-                          fine_group=wl.fine_group, fine_keep=wl.fine_keep)
-    return prob, pol
+from block_sparse_attention_tile_amd.workload import flags_of, plan_structs as structs_of  # noqa: E402,F401
 
 
 def oracle_tile_rows(wl, q_h, k_h, tile):
