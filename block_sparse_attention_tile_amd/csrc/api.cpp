@@ -302,7 +302,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     if (f & VSA_SICS_SELECT) {
       sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;
       sz[VSA_WS_TILE_SICS] = (size_t)BH * g.nb * 2 * g.max_tiles * 4;
-      sz[VSA_WS_ATOMS] = (size_t)BH * 2 * g.n_atoms * g.d * 4;
+      sz[VSA_WS_ATOMS] = (size_t)BH * 2 * g.n_atoms * (g.d + 1) * 4;  // sums + non-zero counts
     }
   } else {
     sz[VSA_WS_FINE_QBAR] = (size_t)BH * g.fine_G * g.d * 4;

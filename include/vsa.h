@@ -131,7 +131,7 @@ typedef struct vsa_plan_info {
 #define VSA_WS_CAND        7  /* int32 [B*H] chosen blocking */
 #define VSA_WS_CAND_SCORE  8  /* fp32 [B*H][n_blockings] mean pair cosine */
 #define VSA_WS_TILE_SICS   9  /* fp32 [B*H][n_blockings][2][max_tiles] SICS of Q, K */
-#define VSA_WS_ATOMS      10  /* fp32 SICS partial sums of unit vectors */
+#define VSA_WS_ATOMS      10  /* fp32 [B*H][2][atoms][d] unit-vector sums, then int32 [B*H][2][atoms] non-zero counts */
 #define VSA_WS_FINE_QBAR  11  /* fp32 [B*H][G][d] group means of Q */
 #define VSA_WS_FINE_TAU   12  /* fp64 [B*H] per-head score threshold */
 #define VSA_WS_FINE_COUNT 13  /* int32 [B*H][G] kept keys per group */

@@ -1,0 +1,125 @@
+"""GPU parity of the SICS blocking choice (Wan-14B path) against the oracle.
+
+Tolerances: per-tile SICS and candidate scores 1e-3 relative (absolute floor
+1e-3 x pairs for tiles whose sum cancels); the chosen blocking exact (the
+score margin between the two best candidates is printed); kept tiles
+bit-exact under the chosen blocking; O max-abs <= 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_tile_amd as vsa
+from block_sparse_attention_tile_amd import _lib
+from oracle import attention, geometry, sics
+from synth import CONFIGS, Workload, smooth_field_qkv
+from tests.helpers import csr_rows, oracle_tile_rows, structs_of
+
+pytestmark = pytest.mark.gpu
+ATOL = 2e-2
+CANDS = ((1, 16, 16), (7, 4, 4), (3, 8, 8))
+
+SMALL = {
+    "sics_d128": Workload("sics_d128", 1, 4, 128, (14, 16, 16), (1, 16, 16), candidates=CANDS,
+                          topk_frac=0.2, ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0)),
+    # ragged: H=20 is not a multiple of 16 or 8; two batches; d=64; window too
+    "sics_ragged_d64": Workload("sics_ragged_d64", 2, 2, 64, (7, 20, 16), (1, 16, 16),
+                                candidates=((1, 16, 16), (7, 4, 4)), topk_frac=0.25,
+                                window=(1, 1, 3), ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0)),
+}
+
+
+def _say(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def _check_head(wl, plan, qn, kn, bh, sics_t, scores, cand, row_ptr, col, tol_log):
+    for c, tile in enumerate(wl.candidates):
+        mem = geometry.tile_members(wl.grid, tile)
+        for x, arr in ((0, qn), (1, kn)):
+            ref = sics.tile_sics(arr, mem)
+            got = sics_t[bh, c, x, :len(mem)]
+            pairs = np.array([len(m) * (len(m) - 1) / 2.0 for m in mem])
+            err = np.abs(got - ref)
+            assert np.all(err <= 1e-3 * np.maximum(np.abs(ref), pairs * 1.0)), (bh, c, x, err.max())
+    want_c, sc = sics.candidate_scores(qn, kn, wl.grid, wl.candidates), None
+    ref_scores = want_c
+    assert np.allclose(scores[bh], ref_scores, rtol=1e-3, atol=1e-4), (bh, scores[bh], ref_scores)
+    order = np.sort(ref_scores)[::-1]
+    margin = order[0] - order[1] if len(order) > 1 else np.inf
+    tol_log.append(margin)
+    best = sics.choose(ref_scores)
+    if margin > 1e-4:
+        assert cand[bh] == best, (bh, cand[bh], best, ref_scores)
+    return int(cand[bh])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sics_choice_selection_attention(name):
+    wl = SMALL[name]
+    _say(f"sics {name}")
+    q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=1, device="cuda")
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    o = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    nb = len(wl.candidates)
+    BH = wl.B * wl.H
+    mt = plan.info.max_tiles
+    sics_t = plan.region(_lib.VSA_WS_TILE_SICS, torch.float32).view(BH, nb, 2, mt).cpu().numpy()
+    scores = plan.region(_lib.VSA_WS_CAND_SCORE, torch.float32).view(BH, nb).cpu().numpy()
+    row_ptr, col, cand = plan.read_selection()
+    qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
+    on = o.float().cpu().numpy()
+    margins = []
+    chosen = []
+    for b in range(wl.B):
+        for h in range(wl.H):
+            bh = b * wl.H + h
+            c = _check_head(wl, plan, qn[b, h], kn[b, h], bh, sics_t, scores, cand, row_ptr, col,
+                            margins)
+            chosen.append(c)
+            tile = wl.candidates[c]
+            rows, tmarg, mem = oracle_tile_rows(wl, qn[b, h], kn[b, h], tile)
+            got = csr_rows(row_ptr, col, bh, mt, len(mem))
+            assert got == rows, (b, h)
+            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, got)
+            err = np.abs(on[b, h] - ref).max()
+            assert err <= ATOL, (b, h, err)
+    print(f"chosen blockings {chosen}, min score margin {min(margins):.3e}", flush=True)
+    # heads alternate between temporal and spatial correlation; the choice follows
+    assert chosen[0] != chosen[1]
+
+
+def test_wan14b_full_size():
+    wl = CONFIGS["wan14b"]
+    _say("wan14b full size")
+    q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=0, device="cuda")
+    prob, pol = structs_of(wl)
+    plan = vsa.Plan(prob, pol)
+    o = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    nb = len(wl.candidates)
+    mt = plan.info.max_tiles
+    scores = plan.region(_lib.VSA_WS_CAND_SCORE, torch.float32).view(wl.H, nb).cpu().numpy()
+    sics_t = plan.region(_lib.VSA_WS_TILE_SICS, torch.float32).view(wl.H, nb, 2, mt).cpu().numpy()
+    row_ptr, col, cand = plan.read_selection()
+    margins = []
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.choice(wl.H, 6, replace=False).tolist()) | {0, 1})
+    for h in sample:
+        qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
+        c = _check_head(wl, plan, qn, kn, h, sics_t, scores, cand, row_ptr, col, margins)
+        tile = wl.candidates[c]
+        rows, _, mem = oracle_tile_rows(wl, qn, kn, tile)
+        got = csr_rows(row_ptr, col, h, mt, len(mem))
+        assert got == rows, h
+        assert all(len(r) == plan.info.topk[c] for r in got)
+        on = o[0, h].float().cpu().numpy()
+        tiles = sorted(set(rng.choice(len(mem), 4, replace=False).tolist()) | {len(mem) - 1})
+        ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+        for i in tiles:
+            err = np.abs(on[mem[i]] - ref[mem[i]]).max()
+            assert err <= ATOL, (h, i, err)
+    print(f"cand per head {cand.tolist()}, min margin {min(margins):.3e}", flush=True)
+    assert set(cand[0::2].tolist()) == {1} and set(cand[1::2].tolist()) == {0}
