@@ -33,7 +33,7 @@ VSA_MAX_CAND = 4
 (VSA_WS_QT, VSA_WS_KT, VSA_WS_VT, VSA_WS_POOLED_Q, VSA_WS_POOLED_K, VSA_WS_ROW_LEN,
  VSA_WS_COL_IDX, VSA_WS_CAND, VSA_WS_CAND_SCORE, VSA_WS_TILE_SICS, VSA_WS_ATOMS,
  VSA_WS_FINE_QBAR, VSA_WS_FINE_TAU, VSA_WS_FINE_COUNT, VSA_WS_FINE_IDX, VSA_WS_FINE_PTR,
- VSA_WS_SCRATCH, VSA_WS_NREGIONS) = range(18)
+ VSA_WS_FINE_SCORE, VSA_WS_SCRATCH, VSA_WS_NREGIONS) = range(19)
 
 EXPORTED = [
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_workspace_bytes",

@@ -111,6 +111,7 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.fine_count = (int*)at(VSA_WS_FINE_COUNT);
   w.fine_idx = (int*)at(VSA_WS_FINE_IDX);
   w.fine_ptr = (int*)at(VSA_WS_FINE_PTR);
+  w.fine_score = (double*)at(VSA_WS_FINE_SCORE);
   w.scratch = (unsigned char*)at(VSA_WS_SCRATCH);
   return w;
 }
@@ -310,8 +311,9 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     sz[VSA_WS_FINE_COUNT] = (size_t)BH * g.fine_G * 4;
     sz[VSA_WS_FINE_IDX] = (size_t)BH * g.fine_cap * 4;
     sz[VSA_WS_FINE_PTR] = (size_t)BH * (g.fine_G + 1) * 4;
+    sz[VSA_WS_FINE_SCORE] = (size_t)BH * g.fine_G * (size_t)N * 8;
   }
-  sz[VSA_WS_SCRATCH] = 4096 + (size_t)BH * 64 * 1024 * 4;  // counters + histograms
+  sz[VSA_WS_SCRATCH] = (f & VSA_FINE) ? vsa::fine_scratch_bytes(g) : 256;
   size_t offv = 0;
   for (int r = 0; r < VSA_WS_NREGIONS; ++r) {
     p->off[r] = sz[r] ? offv : 0;

@@ -31,32 +31,18 @@
 //    the same XCD and its L2.
 #include <hip/hip_runtime.h>
 
+#include "attn_core.h"
 #include "vsa_internal.h"
 
 namespace vsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using core::kKC;
+using core::Lds;
+using core::u32x4;
 
 constexpr int kMaxWaves = 8;
-constexpr int kKC = 64;                       // keys per chunk
 constexpr int kNumXcd = 8;
-
-template <int D>
-struct Lds {
-  static constexpr int KS = D + 8;            // K row stride (bf16), +16 B: conflict-free b128 reads
-  static constexpr int VS = kKC + 8;          // V^T row stride (bf16)
-  static constexpr int KE = kKC * KS;         // K elements per stage
-  static constexpr int VE = D * VS;           // V^T elements per stage
-  static constexpr int STAGE = KE + VE;
-};
-
-__device__ __forceinline__ int key_perm(int m) {
-  // swap bits 2 and 3 of a row index inside a 32-row block
-  return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
 
 struct TileInfo {
   int it, ih, iw, et, eh, ew, nvalid;
@@ -164,8 +150,6 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
                                                          uint16_t* __restrict__ o, int nsb,
                                                          int n_items) {
   extern __shared__ __align__(16) uint16_t lds[];
-  constexpr int DK = D / 16;   // MFMA k-steps over the head dimension
-  constexpr int DT = D / 32;   // 32-row blocks of O^T
 
   // XCD-major mapping of workgroups to work items.
   const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
@@ -191,22 +175,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
   const long head_tm = bh * g.tok_cap * D;
   const TileInfo ti = tinfo(g, b, i);
 
-  // Q fragments: B operand (k = head dim, n = query).
-  bf16x8 qf[DK];
-  if (active) {
-    const uint16_t* qp = qt + head_tm + ((long)i * slots + qrow + col) * D + hi * 8;
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-  }
-
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  core::WaveState<D> ws;
+  if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
-  float m_run = -INFINITY;
-  float l_part = 0.f;
 
   const int L = row_len[bh * g.max_tiles + i];
   const int* cols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
@@ -248,80 +219,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
     const ChunkIter nxt = advance(cur);
     const bool has_next = nxt.e < L;
     if (has_next) ld.load(kt, vt, head_tm, slots, nxt.j, nxt.off, rows_of(nxt));
-
     const uint16_t* lk = lds + stage * Lds<D>::STAGE;
-    const uint16_t* lvt = lk + Lds<D>::KE;
-    const int ck = min(kKC, cur.nv - cur.off);   // valid keys in this chunk
-    const int nmt = ck > 32 ? 2 : 1;
-
-    if (active) {
-      // S^T = K Q^T for up to two 32-key blocks.
-      f32x16 s[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nmt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-          const uint16_t* kp = lk + (mt * 32 + key_perm(col)) * Lds<D>::KS + hi * 8;
-#pragma unroll
-          for (int kk = 0; kk < DK; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
-            s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
-          }
-        }
-      }
-      // Mask keys beyond the tile's valid count; key of reg r in block mt is
-      // mt*32 + 16*(r/8) + 8*hi + r%8.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nmt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-            if (key >= ck) s[mt][r] = -INFINITY;
-            mx = fmaxf(mx, s[mt][r]);
-          }
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const bool need = (m_new - m_run) * c2 > 8.0f;
-      if (__any(need)) {
-        const float alpha = exp2f((m_run - m_new) * c2);
-        l_part *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = m_run * c2;
-      // P^T (bf16) as B operand, and PV.
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nmt) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            bf16x8 pb;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const float pv = exp2f(fmaf(s[mt][half * 8 + t], c2, -mc));
-              l_part += pv;
-              pb[t] = (__bf16)pv;
-            }
-            const int ks = mt * 2 + half;   // 16-key step inside the chunk
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              const bf16x8 a = *reinterpret_cast<const bf16x8*>(lvt + (dt * 32 + col) * Lds<D>::VS +
-                                                                 ks * 16 + hi * 8);
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-
+    if (active) ws.chunk(lk, lk + Lds<D>::KE, min(kKC, cur.nv - cur.off), c2, col, hi);
     if (has_next) ld.store(lds + (stage ^ 1) * Lds<D>::STAGE);
     __syncthreads();
     stage ^= 1;
@@ -330,24 +229,9 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
 
   if (!active) return;
   const int qs = qrow + col;  // slot of this lane's query
-  if (qs >= ti.nvalid) return;
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* op = o + (bh * (long)g.N + token_of(g, b, ti, qs)) * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = dt * 32 + 8 * r4 + 4 * hi;
-      __bf16 h[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[dt][4 * r4 + x] * inv);
-      uint2 pk;
-      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
-      *reinterpret_cast<uint2*>(op + d0) = pk;
-    }
-  }
+  const bool valid = qs < ti.nvalid;
+  uint16_t* op = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
+  ws.store(op, hi, valid);
 }
 
 template <int D, int NW>

@@ -1,0 +1,161 @@
+// Per-wave flash-attention core shared by the tile and the fine-grained
+// attention kernels (CDNA4 / gfx950, v_mfma_f32_32x32x16_bf16).
+//
+// A wave owns 32 query rows.  For each chunk of up to 64 keys staged in LDS
+// (K row-major, V transposed [d][key]) it computes S^T = K Q^T, masks keys
+// past the chunk's valid count, updates the online softmax (running max and
+// sum; the result equals masked softmax attention, SPADE review page,
+// ledger axiom on FlashAttention-style online softmax) and accumulates
+// O^T += V^T P^T.
+//
+// Lane layout (32x32x16 MFMA): output column = lane % 32, so each lane owns
+// one query; its 16 accumulator registers hold rows 8*(r/4) + 4*(lane/32) +
+// r%4.  K rows are fed in the order key_perm(row) (bits 2 and 3 swapped), so
+// register r of key block mt holds key mt*32 + 16*(r/8) + 8*(lane/32) + r%8:
+// eight consecutive keys per lane half, exactly the B-operand layout of the
+// P^T V^T product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace vsa {
+namespace core {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKC = 64;  // keys per chunk
+
+template <int D>
+struct Lds {
+  static constexpr int KS = D + 8;     // K row stride (bf16); +16 B keeps b128 reads conflict-free
+  static constexpr int VS = kKC + 8;   // V^T row stride (bf16)
+  static constexpr int KE = kKC * KS;  // K elements per stage
+  static constexpr int VE = D * VS;    // V^T elements per stage
+  static constexpr int STAGE = KE + VE;
+};
+
+__device__ __forceinline__ int key_perm(int m) {
+  return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+template <int D>
+struct WaveState {
+  static constexpr int DK = D / 16;  // MFMA k-steps over the head dimension
+  static constexpr int DT = D / 32;  // 32-row blocks of O^T
+  bf16x8 qf[DK];                     // Q fragment (B operand: k = head dim, n = query)
+  f32x16 acc[DT];                    // O^T accumulators
+  float m_run;                       // running max (raw score units)
+  float l_part;                      // this lane half's partial row sum
+
+  __device__ __forceinline__ void init(const uint16_t* qrow_ptr, int hi) {
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow_ptr + kk * 16 + hi * 8);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    m_run = -INFINITY;
+    l_part = 0.f;
+  }
+
+  // One chunk: ck valid keys (1..64) at the start of the staged chunk.
+  // c2 = softmax scale * log2(e).
+  __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
+                                        int col, int hi) {
+    const int nmt = ck > 32 ? 2 : 1;
+    f32x16 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt < nmt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+        const uint16_t* kp = lk + (mt * 32 + key_perm(col)) * Lds<D>::KS + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt < nmt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+          if (key >= ck) s[mt][r] = -INFINITY;
+          mx = fmaxf(mx, s[mt][r]);
+        }
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy rescaling: raise the running max only when a score exceeds it by
+    // more than 2^8 in exp2 units; probabilities stay <= 256 and the final
+    // normalisation by the same running sum is exact.
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = (m_new - m_run) * c2 > 8.0f;
+    if (__any(need)) {
+      const float alpha = exp2f((m_run - m_new) * c2);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt < nmt) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 pb;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float pv = exp2f(fmaf(s[mt][half * 8 + t], c2, -mc));
+            l_part += pv;
+            pb[t] = (__bf16)pv;
+          }
+          const int ks = mt * 2 + half;  // 16-key step inside the chunk
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(lvt + (dt * 32 + col) * Lds<D>::VS + ks * 16 + hi * 8);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // Normalise and write this lane's query row (d channels, bf16) to op.
+  // Must be called by both lane halves (they exchange their partial sums).
+  __device__ __forceinline__ void store(uint16_t* op, int hi, bool write) {
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    if (!write) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + 8 * r4 + 4 * hi;
+        __bf16 h[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[dt][4 * r4 + x] * inv);
+        uint2 pk;
+        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
+        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+        *reinterpret_cast<uint2*>(op + d0) = pk;
+      }
+    }
+  }
+};
+
+}  // namespace core
+}  // namespace vsa

@@ -75,8 +75,12 @@ struct Ws {
   int* fine_count;
   int* fine_idx;
   int* fine_ptr;
+  double* fine_score;
   unsigned char* scratch;
 };
+
+// Bytes of internal scratch the fine-grained mask needs (fine.hip).
+size_t fine_scratch_bytes(const Geo& g);
 
 // Kernel launchers (kernels.hip / sics.hip / fine.hip); return hipError_t.
 hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,

@@ -137,8 +137,9 @@ typedef struct vsa_plan_info {
 #define VSA_WS_FINE_COUNT 13  /* int32 [B*H][G] kept keys per group */
 #define VSA_WS_FINE_IDX   14  /* int32 [B*H][fine_cap] kept keys, groups in order */
 #define VSA_WS_FINE_PTR   15  /* int32 [B*H][G+1] start of each group's keys */
-#define VSA_WS_SCRATCH    16  /* internal */
-#define VSA_WS_NREGIONS   17
+#define VSA_WS_FINE_SCORE 16  /* fp64 [B*H][G][N] group-key scores */
+#define VSA_WS_SCRATCH    17  /* internal */
+#define VSA_WS_NREGIONS   18
 
 /* ---- plan ---------------------------------------------------------------
  * Validates `prob` and `pol`, computes the tile geometry of every blocking,
