@@ -12,9 +12,9 @@
 //  * One workgroup = NW waves = NW*32 query rows of one query tile; a wave
 //    owns 32 query rows for the whole KV sweep (its Q fragment stays in
 //    VGPRs).
-//  * K and V^T are streamed in chunks of 64 (or a final 32) keys through LDS,
-//    double-buffered: the global loads of chunk c+1 are in flight while chunk
-//    c is multiplied.
+//  * K and V^T are streamed in chunks of 64 (or a final 32) keys through LDS
+//    with direct global->LDS loads, double-buffered: chunk c+1 is in flight
+//    while chunk c is multiplied.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the output column is the
 //    query, so each lane owns one query and 16 keys and the softmax row
 //    reductions are lane-local (plus one swap between the wave halves).
@@ -39,9 +39,8 @@ namespace {
 
 using core::kKC;
 using core::Lds;
-using core::u32x4;
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 4;
 constexpr int kNumXcd = 8;
 
 struct TileInfo {
@@ -86,61 +85,65 @@ struct ChunkIter {
   int nv;     // valid keys of tile j
 };
 
-template <int D, int NW>
-struct Loader {
-  // per thread: K pieces + V^T pieces of one 64-key chunk
-  static constexpr int KP = kKC * (D / 8);        // 16-byte pieces of K
-  static constexpr int VP = D * (kKC / 8);        // 16-byte pieces of V^T
-  static constexpr int T = NW * 64;
-  static constexpr int NK = (KP + T - 1) / T;
-  static constexpr int NV = (VP + T - 1) / T;
-  u32x4 kr[NK];
-  u32x4 vr[NV];
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-  // Unconditional loads from clamped, always in-bounds addresses keep the
-  // staging arrays in VGPRs: pieces past `rows` (a 32-key chunk) re-read the
-  // last valid row and are never used, pieces past the chunk duplicate the
-  // last piece.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                       long head_tm, int slots, int j, int off, int rows) {
-    const int tid = threadIdx.x;
-    const uint16_t* kbase = kt + head_tm + ((long)j * slots + off) * D;
-    const uint16_t* vbase = vt + head_tm + (long)j * D * slots + off;
+// Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
+// Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
+// the lane's global source is picked so that LDS ends up in the swizzled
+// layout of Lds<D>.  The per-lane source offsets depend only on the lane and
+// the tile's slot count, so they are computed once per kernel.  A 32-key
+// chunk skips the K instructions of rows 32..63 and the V^T lanes of keys
+// 32..63, so every access stays inside the tile.  No VGPR staging and no LDS
+// stores: the data is in flight while the previous chunk is multiplied.
+template <int D, int NW>
+struct ChunkLoader {
+  static constexpr int KI = Lds<D>::KC16;    // K instructions (1 KB each)
+  static constexpr int VI = D / 8;           // V^T instructions
+  static constexpr int NI = KI + VI;
+  static constexpr int PER = (NI + NW - 1) / NW;
+  int off[PER];        // source element offset inside the chunk's tile data
+  unsigned vhi;        // bit x: this lane's V^T piece of instruction x holds keys 32..63
+
+  __device__ __forceinline__ void init(int wave, int lane, int slots) {
+    vhi = 0;
 #pragma unroll
-    for (int x = 0; x < NK; ++x) {
-      const int pc = min(tid + x * T, KP - 1);
-      const int r = min(pc / (D / 8), rows - 1), p = pc % (D / 8);
-      kr[x] = *reinterpret_cast<const u32x4*>(kbase + (long)r * D + p * 8);
-    }
-#pragma unroll
-    for (int x = 0; x < NV; ++x) {
-      const int pc = min(tid + x * T, VP - 1);
-      const int dd = pc / (kKC / 8), p = min(pc % (kKC / 8), rows / 8 - 1);
-      vr[x] = *reinterpret_cast<const u32x4*>(vbase + (long)dd * slots + p * 8);
+    for (int x = 0; x < PER; ++x) {
+      const int ins = wave + x * NW;
+      const int P = ins * 64 + lane;
+      if (ins < KI) {
+        const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
+        const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
+        off[x] = r * D + c * 8;
+      } else {
+        const int Pv = P - KI * 64;
+        const int d = Pv / 8, pc = Pv % 8;
+        const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
+        off[x] = d * slots + c * 8;
+        if (c >= 4) vhi |= 1u << x;
+      }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* lds) {
-    const int tid = threadIdx.x;
-    uint16_t* lk = lds;
-    uint16_t* lvt = lds + Lds<D>::KE;
+  __device__ __forceinline__ void issue(uint16_t* stage, const uint16_t* __restrict__ kbase,
+                                        const uint16_t* __restrict__ vbase, bool half, int wave) const {
 #pragma unroll
-    for (int x = 0; x < NK; ++x) {
-      const int pc = min(tid + x * T, KP - 1);
-      const int r = pc / (D / 8), p = pc % (D / 8);
-      *reinterpret_cast<u32x4*>(lk + r * Lds<D>::KS + p * 8) = kr[x];
-    }
-#pragma unroll
-    for (int x = 0; x < NV; ++x) {
-      const int pc = min(tid + x * T, VP - 1);
-      const int dd = pc / (kKC / 8), p = pc % (kKC / 8);
-      *reinterpret_cast<u32x4*>(lvt + dd * Lds<D>::VS + p * 8) = vr[x];
+    for (int x = 0; x < PER; ++x) {
+      const int ins = wave + x * NW;
+      if (ins >= NI) break;
+      if (ins < KI) {
+        if (half && ins * 64 / Lds<D>::KC16 >= 32) continue;
+        __builtin_amdgcn_global_load_lds(kbase + off[x], (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
+      } else if (!(half && ((vhi >> x) & 1u))) {
+        __builtin_amdgcn_global_load_lds(vbase + off[x], (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
+      }
     }
   }
 };
 
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
+__global__ __launch_bounds__(NW * 64, 2) void attend_kernel(Geo g, int blocking,
                                                          const uint16_t* __restrict__ qt,
                                                          const uint16_t* __restrict__ kt,
                                                          const uint16_t* __restrict__ vt,
@@ -207,21 +210,25 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(Geo g, int blocking,
     return it;
   };
 
-  Loader<D, NW> ld;
   int stage = 0;
-  if (L > 0) {
-    ld.load(kt, vt, head_tm, slots, cur.j, cur.off, rows_of(cur));
-    ld.store(lds);
-  }
+  const uint16_t* kt_head = kt + head_tm;
+  const uint16_t* vt_head = vt + head_tm;
+  auto kaddr = [&](const ChunkIter& it) { return kt_head + ((long)it.j * slots + it.off) * D; };
+  auto vaddr = [&](const ChunkIter& it) { return vt_head + (long)it.j * D * slots + it.off; };
+  ChunkLoader<D, NW> ldr;
+  ldr.init(wave, lane, slots);
+  if (L > 0) ldr.issue(lds, kaddr(cur), vaddr(cur), rows_of(cur) == 32, wave);
+  wait_loads();
   __syncthreads();
 
   while (cur.e < L) {
     const ChunkIter nxt = advance(cur);
     const bool has_next = nxt.e < L;
-    if (has_next) ld.load(kt, vt, head_tm, slots, nxt.j, nxt.off, rows_of(nxt));
+    if (has_next)
+      ldr.issue(lds + (stage ^ 1) * Lds<D>::STAGE, kaddr(nxt), vaddr(nxt), rows_of(nxt) == 32, wave);
     const uint16_t* lk = lds + stage * Lds<D>::STAGE;
     if (active) ws.chunk(lk, lk + Lds<D>::KE, min(kKC, cur.nv - cur.off), c2, col, hi);
-    if (has_next) ld.store(lds + (stage ^ 1) * Lds<D>::STAGE);
+    wait_loads();
     __syncthreads();
     stage ^= 1;
     cur = nxt;

@@ -2,7 +2,7 @@
 // attention kernels (CDNA4 / gfx950, v_mfma_f32_32x32x16_bf16).
 //
 // A wave owns 32 query rows.  For each chunk of up to 64 keys staged in LDS
-// (K row-major, V transposed [d][key]) it computes S^T = K Q^T, masks keys
+// (K by key rows, V transposed [d][key], both swizzled) it computes S^T = K Q^T, masks keys
 // past the chunk's valid count, updates the online softmax (running max and
 // sum; the result equals masked softmax attention, SPADE review page,
 // ledger axiom on FlashAttention-style online softmax) and accumulates
@@ -24,21 +24,39 @@ namespace core {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kKC = 64;  // keys per chunk
-
-template <int D>
-struct Lds {
-  static constexpr int KS = D + 8;     // K row stride (bf16); +16 B keeps b128 reads conflict-free
-  static constexpr int VS = kKC + 8;   // V^T row stride (bf16)
-  static constexpr int KE = kKC * KS;  // K elements per stage
-  static constexpr int VE = D * VS;    // V^T elements per stage
-  static constexpr int STAGE = KE + VE;
-};
 
 __device__ __forceinline__ int key_perm(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
+
+
+// LDS stage: K chunk [64 keys][D] and V^T chunk [D][64 keys], bf16, rows
+// unpadded so that a wave's 64 x 16-byte direct global->LDS load fills 1 KB
+// contiguously.  Bank conflicts of the 16-byte fragment reads are avoided by
+// XOR-swizzling the 16-byte column index with a function of the row chosen
+// so that any 8 (and any 16) consecutive lanes of a fragment read touch
+// distinct bank groups.
+template <int D>
+struct Lds {
+  static constexpr int KE = kKC * D;       // K elements per stage
+  static constexpr int VE = D * kKC;       // V^T elements per stage
+  static constexpr int STAGE = KE + VE;
+  static constexpr int KC16 = D / 8;       // 16-byte columns per K row
+  static constexpr int VC16 = kKC / 8;     // 16-byte columns per V^T row (8)
+  // K row r (key), 16-byte column c -> element offset
+  __device__ __forceinline__ static int k_off(int r, int c) {
+    return r * D + ((c ^ (key_perm(r & 31) & (KC16 - 1))) << 3);
+  }
+  // V^T row d (channel), 16-byte column c (8 keys) -> element offset
+  __device__ __forceinline__ static int v_off(int d, int c) {
+    return d * kKC + ((c ^ ((d & 7) ^ ((d >> 3) & 1))) << 3);
+  }
+};
 
 template <int D>
 struct WaveState {
@@ -70,28 +88,36 @@ struct WaveState {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       if (mt < nmt) {
+        const int row = mt * 32 + key_perm(col);
+        bf16x8 a[DK];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-        const uint16_t* kp = lk + (mt * 32 + key_perm(col)) * Lds<D>::KS + hi * 8;
+        for (int kk = 0; kk < DK; ++kk)
+          a[kk] = *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi));
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mt], 0, 0, 0);
+        for (int kk = 1; kk < DK; ++kk)
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qf[kk], s[mt], 0, 0, 0);
+      }
+    }
+    // Keys past the chunk's valid count (only in a tile's last chunk).
+    if (ck < kKC) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        if (mt < nmt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
+            if (key >= ck) s[mt][r] = -INFINITY;
+          }
         }
       }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (mt < nmt) {
+    for (int mt = 0; mt < 2; ++mt)
+      if (mt < nmt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-          if (key >= ck) s[mt][r] = -INFINITY;
-          mx = fmaxf(mx, s[mt][r]);
-        }
-      }
-    }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescaling: raise the running max only when a score exceeds it by
     // more than 2^8 in exp2 units; probabilities stay <= 256 and the final
@@ -99,7 +125,7 @@ struct WaveState {
     const float m_new = fmaxf(m_run, mx);
     const bool need = (m_new - m_run) * c2 > 8.0f;
     if (__any(need)) {
-      const float alpha = exp2f((m_run - m_new) * c2);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -115,18 +141,22 @@ struct WaveState {
         for (int half = 0; half < 2; ++half) {
           bf16x8 pb;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float pv = exp2f(fmaf(s[mt][half * 8 + t], c2, -mc));
-            l_part += pv;
-            pb[t] = (__bf16)pv;
+          for (int t = 0; t < 8; ++t)
+            pb[t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mt][half * 8 + t], c2, -mc));
+          // row sum of the rounded probabilities actually multiplied with V
+#pragma unroll
+          for (int t = 0; t < 8; t += 2) {
+            bf16x2 pr = {pb[t], pb[t + 1]};
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
           }
           const int ks = mt * 2 + half;  // 16-key step inside the chunk
+          bf16x8 a[DT];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(lvt + (dt * 32 + col) * Lds<D>::VS + ks * 16 + hi * 8);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dt], 0, 0, 0);
-          }
+          for (int dt = 0; dt < DT; ++dt)
+            a[dt] = *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi));
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb, acc[dt], 0, 0, 0);
         }
       }
     }

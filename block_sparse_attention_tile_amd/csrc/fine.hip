@@ -363,20 +363,21 @@ struct GatherLoader {
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
       const int pc = min(tid + x * T, kKC * P - 1);
-      *reinterpret_cast<u32x4*>(lk + (pc / P) * Lds<D>::KS + (pc % P) * 8) = kr[x];
+      *reinterpret_cast<u32x4*>(lk + Lds<D>::k_off(pc / P, pc % P)) = kr[x];
       const int r = pc % kKC, p = pc / kKC;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t w = vr[x][e];
-        lvt[(p * 8 + 2 * e) * Lds<D>::VS + r] = (uint16_t)(w & 0xffffu);
-        lvt[(p * 8 + 2 * e + 1) * Lds<D>::VS + r] = (uint16_t)(w >> 16);
+        const int d0 = p * 8 + 2 * e;
+        lvt[Lds<D>::v_off(d0, r >> 3) + (r & 7)] = (uint16_t)(w & 0xffffu);
+        lvt[Lds<D>::v_off(d0 + 1, r >> 3) + (r & 7)] = (uint16_t)(w >> 16);
       }
     }
   }
 };
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fine_attend_kernel(Geo g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               const int* __restrict__ ptr,
