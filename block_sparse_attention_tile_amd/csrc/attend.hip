@@ -9,21 +9,17 @@
 // dense compute, every computed block is dense).
 //
 // Design for gfx950:
-//  * One workgroup = NW waves = NW*32 query rows of one query tile; a wave
-//    owns 32 query rows for the whole KV sweep (its Q fragment stays in
-//    VGPRs).
-//  * K and V^T are streamed in chunks of 64 (or a final 32) keys through LDS
-//    with direct global->LDS loads, double-buffered: chunk c+1 is in flight
-//    while chunk c is multiplied.
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the output column is the
-//    query, so each lane owns one query and 16 keys and the softmax row
-//    reductions are lane-local (plus one swap between the wave halves).
-//  * A-operand rows of K are read in a permuted order (bits 2 and 3 of the
-//    row swapped) so that the fp32 S^T accumulator, converted to bf16, is
-//    already the B operand of the next MFMA: O^T += V^T P^T.
-//  * Lazy rescaling: the running max is only raised (and O rescaled) when a
-//    new score exceeds it by more than 2^8 in exp2 units, which keeps every
-//    probability <= 256 and is exact in the final normalisation.
+//  * One workgroup covers a whole query tile when it has at most 12 slabs of
+//    32 rows (a 384-token tile is 12 waves, 3 per SIMD), so every K/V chunk
+//    crosses from L2 into LDS once per query tile.  A wave owns 32 query rows
+//    for the whole KV sweep; its Q fragment stays in VGPRs.
+//  * K and V^T stream in chunks of 64 (or a final 32) keys through a ring of
+//    LDS stages filled by direct global->LDS loads (no VGPR staging); up to
+//    STAGES-1 chunks are in flight while one is multiplied, and the wait for
+//    a chunk counts only the loads issued before it (s_waitcnt vmcnt(n)).
+//  * The kept-tile list is copied to LDS first, so the loop issues no other
+//    global loads that would drain the queue.
+//  * The MFMA / online-softmax math per 32-key block is in attn_core.h.
 //  * The epilogue writes O straight to the raster layout (the inverse
 //    permutation is fused here), skipping padded query slots.
 //  * Workgroups are mapped XCD-major: consecutive work items (same head,
@@ -40,7 +36,7 @@ namespace {
 using core::kKC;
 using core::Lds;
 
-constexpr int kMaxWaves = 4;
+constexpr int kMaxWaves = 12;
 constexpr int kNumXcd = 8;
 
 struct TileInfo {
@@ -77,49 +73,70 @@ __device__ __forceinline__ long token_of(const Geo& g, const BlkGeo& b, const Ti
          (t.iw * b.tile[2] + sw);
 }
 
-// Iterator over the key chunks of one query tile's kept list.
-struct ChunkIter {
-  int e;      // position in the kept list
-  int j;      // key tile
-  int off;    // first slot of the chunk inside tile j
-  int nv;     // valid keys of tile j
-};
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Iterator over the 64-key chunks of a query tile's kept key tiles (read
+// from the LDS copy of the list).
+struct ChunkIter {
+  int e;    // position in the kept list
+  int j;    // key tile
+  int off;  // first slot of the chunk inside tile j
+  int nv;   // valid keys of tile j
+  __device__ __forceinline__ void start(const int* cols, int L, const Geo& g, const BlkGeo& b) {
+    e = 0;
+    off = 0;
+    j = L > 0 ? cols[0] : 0;
+    nv = L > 0 ? tile_nvalid(g, b, j) : 0;
+  }
+  __device__ __forceinline__ void next(const int* cols, int L, const Geo& g, const BlkGeo& b) {
+    off += kKC;
+    if (off >= nv) {
+      off = 0;
+      if (++e < L) {
+        j = cols[e];
+        nv = tile_nvalid(g, b, j);
+      }
+    }
+  }
+  __device__ __forceinline__ int keys() const { return min(kKC, nv - off); }
+};
 
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
 // Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
 // the lane's global source is picked so that LDS ends up in the swizzled
-// layout of Lds<D>.  The per-lane source offsets depend only on the lane and
-// the tile's slot count, so they are computed once per kernel.  A 32-key
-// chunk skips the K instructions of rows 32..63 and the V^T lanes of keys
-// 32..63, so every access stays inside the tile.  No VGPR staging and no LDS
-// stores: the data is in flight while the previous chunk is multiplied.
+// layout of Lds<D>.  Per-lane source offsets depend only on the lane and the
+// tile's slot count and are computed once.  Every wave issues exactly PER
+// instructions per chunk (waves with fewer real pieces repeat their last
+// one), so a wait can count loads per chunk.  A 32-key chunk clamps the
+// source rows / key columns past 32 to the last valid ones: every access
+// stays inside the tile and the extra LDS slots are never read.
 template <int D, int NW>
 struct ChunkLoader {
-  static constexpr int KI = Lds<D>::KC16;    // K instructions (1 KB each)
-  static constexpr int VI = D / 8;           // V^T instructions
+  static constexpr int KI = Lds<D>::KC16;  // K instructions (1 KB each)
+  static constexpr int VI = D / 8;         // V^T instructions
   static constexpr int NI = KI + VI;
   static constexpr int PER = (NI + NW - 1) / NW;
-  int off[PER];        // source element offset inside the chunk's tile data
-  unsigned vhi;        // bit x: this lane's V^T piece of instruction x holds keys 32..63
+  int off_full[PER];  // source element offsets, 64-key chunk
+  int off_half[PER];  // source element offsets, 32-key chunk
+  int dst[PER];       // LDS element offset inside a stage
 
   __device__ __forceinline__ void init(int wave, int lane, int slots) {
-    vhi = 0;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-      const int ins = wave + x * NW;
+      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
       const int P = ins * 64 + lane;
+      dst[x] = ins * 512;
       if (ins < KI) {
         const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
         const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
-        off[x] = r * D + c * 8;
+        off_full[x] = r * D + c * 8;
+        off_half[x] = min(r, 31) * D + c * 8;
       } else {
         const int Pv = P - KI * 64;
         const int d = Pv / 8, pc = Pv % 8;
         const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
-        off[x] = d * slots + c * 8;
-        if (c >= 4) vhi |= 1u << x;
+        off_full[x] = d * slots + c * 8;
+        off_half[x] = d * slots + min(c, 3) * 8;
       }
     }
   }
@@ -128,31 +145,45 @@ struct ChunkLoader {
                                         const uint16_t* __restrict__ vbase, bool half, int wave) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-      const int ins = wave + x * NW;
-      if (ins >= NI) break;
-      if (ins < KI) {
-        if (half && ins * 64 / Lds<D>::KC16 >= 32) continue;
-        __builtin_amdgcn_global_load_lds(kbase + off[x], (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
-      } else if (!(half && ((vhi >> x) & 1u))) {
-        __builtin_amdgcn_global_load_lds(vbase + off[x], (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
-      }
+      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);
+      const uint16_t* base = ins < KI ? kbase : vbase;
+      const int o = half ? off_half[x] : off_full[x];
+      __builtin_amdgcn_global_load_lds(base + o, (lds_ptr_t)(stage + dst[x]), 16, 0, 0);
     }
   }
 };
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most `later` chunks' loads (PER instructions each) of this
+// wave are outstanding, then barrier.  The count is a small run-time value;
+// s_waitcnt takes an immediate, hence the switch.
+template <int PER>
+__device__ __forceinline__ void wait_chunk_and_barrier(int later) {
+  switch (later * PER) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
+#define VSA_WAIT_CASE(n) \
+  case n: asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory"); break;
+    VSA_WAIT_CASE(1) VSA_WAIT_CASE(2) VSA_WAIT_CASE(3) VSA_WAIT_CASE(4) VSA_WAIT_CASE(5)
+    VSA_WAIT_CASE(6) VSA_WAIT_CASE(7) VSA_WAIT_CASE(8) VSA_WAIT_CASE(9) VSA_WAIT_CASE(10)
+    VSA_WAIT_CASE(12) VSA_WAIT_CASE(14) VSA_WAIT_CASE(15) VSA_WAIT_CASE(16) VSA_WAIT_CASE(18)
+    VSA_WAIT_CASE(20) VSA_WAIT_CASE(21) VSA_WAIT_CASE(24) VSA_WAIT_CASE(28) VSA_WAIT_CASE(30)
+    VSA_WAIT_CASE(32) VSA_WAIT_CASE(36) VSA_WAIT_CASE(40) VSA_WAIT_CASE(42) VSA_WAIT_CASE(48)
+#undef VSA_WAIT_CASE
+    default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attend_kernel(Geo g, int blocking,
-                                                         const uint16_t* __restrict__ qt,
-                                                         const uint16_t* __restrict__ kt,
-                                                         const uint16_t* __restrict__ vt,
-                                                         const int* __restrict__ row_len,
-                                                         const int* __restrict__ col_idx,
-                                                         const int* __restrict__ cand,
-                                                         uint16_t* __restrict__ o, int nsb,
-                                                         int n_items) {
+template <int NW>
+struct Occ {
+  static constexpr int kWavesPerSimd = NW > 8 ? 3 : 2;
+};
+
+template <int D, int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel(
+    Geo g, int blocking, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ kt,
+    const uint16_t* __restrict__ vt, const int* __restrict__ row_len, const int* __restrict__ col_idx,
+    const int* __restrict__ cand, uint16_t* __restrict__ o, int nsb, int n_items) {
   extern __shared__ __align__(16) uint16_t lds[];
+  using Loader = ChunkLoader<D, NW>;
 
   // XCD-major mapping of workgroups to work items.
   const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
@@ -171,77 +202,67 @@ __global__ __launch_bounds__(NW * 64, 2) void attend_kernel(Geo g, int blocking,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;      // query column inside the wave's 32 rows
-  const int hi = lane >> 5;       // wave half
+  const int col = lane & 31;  // query column inside the wave's 32 rows
+  const int hi = lane >> 5;   // wave half
   const int qrow = q0 + wave * 32;
   const bool active = qrow < slots;
   const long head_tm = bh * g.tok_cap * D;
-  const TileInfo ti = tinfo(g, b, i);
+
+  // kept-tile list -> LDS (after the K/V stages)
+  int* cols = reinterpret_cast<int*>(lds + STAGES * Lds<D>::STAGE);
+  const int L = row_len[bh * g.max_tiles + i];
+  const int* gcols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
+  for (int e = tid; e < L; e += NW * 64) cols[e] = gcols[e];
 
   core::WaveState<D> ws;
   if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
+  Loader ldr;
+  ldr.init(wave, lane, slots);
+  __syncthreads();  // cols visible
 
-  const int L = row_len[bh * g.max_tiles + i];
-  const int* cols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
+  // total chunks of the row
+  int total = 0;
+  for (int e = 0; e < L; ++e) total += (tile_nvalid(g, b, cols[e]) + kKC - 1) / kKC;
 
-  // chunk iterator
-  ChunkIter cur;
-  cur.e = 0;
-  cur.off = 0;
-  if (L > 0) {
-    cur.j = cols[0];
-    cur.nv = tile_nvalid(g, b, cur.j);
-  }
-  auto rows_of = [&](const ChunkIter& it) {
-    const int ck = min(kKC, it.nv - it.off);
-    return ck > 32 ? 64 : 32;
-  };
-  auto advance = [&](ChunkIter it) {
-    it.off += kKC;
-    if (it.off >= it.nv) {
-      it.off = 0;
-      ++it.e;
-      if (it.e < L) {
-        it.j = cols[it.e];
-        it.nv = tile_nvalid(g, b, it.j);
-      }
-    }
-    return it;
-  };
-
-  int stage = 0;
   const uint16_t* kt_head = kt + head_tm;
   const uint16_t* vt_head = vt + head_tm;
-  auto kaddr = [&](const ChunkIter& it) { return kt_head + ((long)it.j * slots + it.off) * D; };
-  auto vaddr = [&](const ChunkIter& it) { return vt_head + (long)it.j * D * slots + it.off; };
-  ChunkLoader<D, NW> ldr;
-  ldr.init(wave, lane, slots);
-  if (L > 0) ldr.issue(lds, kaddr(cur), vaddr(cur), rows_of(cur) == 32, wave);
-  wait_loads();
-  __syncthreads();
-
-  while (cur.e < L) {
-    const ChunkIter nxt = advance(cur);
-    const bool has_next = nxt.e < L;
-    if (has_next)
-      ldr.issue(lds + (stage ^ 1) * Lds<D>::STAGE, kaddr(nxt), vaddr(nxt), rows_of(nxt) == 32, wave);
-    const uint16_t* lk = lds + stage * Lds<D>::STAGE;
-    if (active) ws.chunk(lk, lk + Lds<D>::KE, min(kKC, cur.nv - cur.off), c2, col, hi);
-    wait_loads();
-    __syncthreads();
-    stage ^= 1;
-    cur = nxt;
+  ChunkIter ld_it, cur;
+  ld_it.start(cols, L, g, b);
+  cur = ld_it;
+  // prologue: chunks 0 .. STAGES-2
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < total) {
+      ldr.issue(lds + s * Lds<D>::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32, wave);
+      ld_it.next(cols, L, g, b);
+    }
+  }
+  for (int c = 0; c < total; ++c) {
+    // chunk c's loads are done once only the later-issued ones are pending
+    wait_chunk_and_barrier<Loader::PER>(min(STAGES - 2, total - 1 - c));
+    const int nc = c + STAGES - 1;  // refill the stage freed by chunk c-1
+    if (nc < total) {
+      ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
+                kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32, wave);
+      ld_it.next(cols, L, g, b);
+    }
+    const uint16_t* lk = lds + (c % STAGES) * Lds<D>::STAGE;
+    if (active) ws.chunk(lk, lk + Lds<D>::KE, cur.keys(), c2, col, hi);
+    cur.next(cols, L, g, b);
   }
 
   if (!active) return;
+  const TileInfo ti = tinfo(g, b, i);
   const int qs = qrow + col;  // slot of this lane's query
   const bool valid = qs < ti.nvalid;
   uint16_t* op = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
   ws.store(op, hi, valid);
 }
 
-template <int D, int NW>
+template <int D, int NW, int STAGES>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
   const BlkGeo& b = g.blk[blocking];
@@ -249,36 +270,42 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
   const int nsb = (slabs + NW - 1) / NW;
   const long items = (long)g.B * g.H * g.max_tiles * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
-  const size_t shmem = 2 * Lds<D>::STAGE * sizeof(uint16_t);
-  static bool attr_set = false;   // more than 64 KB of dynamic LDS must be requested
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW>),
+  const size_t shmem = (size_t)STAGES * Lds<D>::STAGE * sizeof(uint16_t) + (size_t)g.row_cap * 4;
+  static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
+  if (attr_bytes < shmem) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<D, NW>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s, g,
-                     blocking, w.qt, w.kt, w.vt, w.row_len, w.col_idx, cand, o, nsb, (int)items);
+  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+                     g, blocking, w.qt, w.kt, w.vt, w.row_len, w.col_idx, cand, o, nsb, (int)items);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                     hipStream_t s) {
-  // Waves per workgroup: split the tile's 32-row slabs into as few groups of
-  // at most kMaxWaves as possible, balanced.
+  // Waves per workgroup: the tile's 32-row slabs split into as few balanced
+  // groups of at most kMaxWaves as possible.  Twelve waves (3 per SIMD, one
+  // workgroup per CU) get a 4-stage ring; smaller groups run two workgroups
+  // per CU with 2 stages each.
   const int slabs = g.blk[blocking].slots / 32;
   const int groups = (slabs + kMaxWaves - 1) / kMaxWaves;
   const int nw = (slabs + groups - 1) / groups;
   switch (nw) {
-    case 1: return launch_one<D, 1>(g, w, blocking, cand, o, s);
-    case 2: return launch_one<D, 2>(g, w, blocking, cand, o, s);
-    case 3: return launch_one<D, 3>(g, w, blocking, cand, o, s);
-    case 4: return launch_one<D, 4>(g, w, blocking, cand, o, s);
-    case 5: return launch_one<D, 5>(g, w, blocking, cand, o, s);
-    case 6: return launch_one<D, 6>(g, w, blocking, cand, o, s);
-    case 7: return launch_one<D, 7>(g, w, blocking, cand, o, s);
-    default: return launch_one<D, 8>(g, w, blocking, cand, o, s);
+    case 1: return launch_one<D, 1, 2>(g, w, blocking, cand, o, s);
+    case 2: return launch_one<D, 2, 2>(g, w, blocking, cand, o, s);
+    case 3: return launch_one<D, 3, 2>(g, w, blocking, cand, o, s);
+    case 4: return launch_one<D, 4, 2>(g, w, blocking, cand, o, s);
+    case 5: return launch_one<D, 5, 2>(g, w, blocking, cand, o, s);
+    case 6: return launch_one<D, 6, 2>(g, w, blocking, cand, o, s);
+    case 7: return launch_one<D, 7, 2>(g, w, blocking, cand, o, s);
+    case 8: return launch_one<D, 8, 2>(g, w, blocking, cand, o, s);
+    case 9: return launch_one<D, 9, 4>(g, w, blocking, cand, o, s);
+    case 10: return launch_one<D, 10, 4>(g, w, blocking, cand, o, s);
+    case 11: return launch_one<D, 11, 4>(g, w, blocking, cand, o, s);
+    default: return launch_one<D, 12, 4>(g, w, blocking, cand, o, s);
   }
 }
 

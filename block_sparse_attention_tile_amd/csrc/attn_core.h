@@ -79,52 +79,33 @@ struct WaveState {
     l_part = 0.f;
   }
 
-  // One chunk: ck valid keys (1..64) at the start of the staged chunk.
-  // c2 = softmax scale * log2(e).
-  __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
-                                        int col, int hi) {
-    const int nmt = ck > 32 ? 2 : 1;
-    f32x16 s[2];
+  // One 32-key block (keys kb*32 .. kb*32+31 of the staged chunk), of which
+  // the first nk are valid.  c2 = softmax scale * log2(e).
+  __device__ __forceinline__ void block32(const uint16_t* lk, const uint16_t* lvt, int kb, int nk,
+                                          float c2, int col, int hi) {
+    // S^T = K Q^T for 32 keys x 32 queries
+    const int row = kb * 32 + key_perm(col);
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, hi)), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (mt < nmt) {
-        const int row = mt * 32 + key_perm(col);
-        bf16x8 a[DK];
+    for (int kk = 1; kk < DK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi)), qf[kk], s, 0, 0, 0);
+    // keys past the valid count (only in a tile's last block)
+    if (nk < 32) {
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk)
-          a[kk] = *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi));
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-        for (int kk = 1; kk < DK; ++kk)
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qf[kk], s[mt], 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r)
+        if (16 * (r >> 3) + 8 * hi + (r & 7) >= nk) s[r] = -INFINITY;
     }
-    // Keys past the chunk's valid count (only in a tile's last chunk).
-    if (ck < kKC) {
+    float mx = s[0];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nmt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = mt * 32 + 16 * (r >> 3) + 8 * hi + (r & 7);
-            if (key >= ck) s[mt][r] = -INFINITY;
-          }
-        }
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      if (mt < nmt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescaling: raise the running max only when a score exceeds it by
     // more than 2^8 in exp2 units; probabilities stay <= 256 and the final
     // normalisation by the same running sum is exact.
     const float m_new = fmaxf(m_run, mx);
-    const bool need = (m_new - m_run) * c2 > 8.0f;
-    if (__any(need)) {
+    if (__any((m_new - m_run) * c2 > 8.0f)) {
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_part *= alpha;
 #pragma unroll
@@ -135,31 +116,31 @@ struct WaveState {
     }
     const float mc = m_run * c2;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (mt < nmt) {
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 pb;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 pb;
+      for (int t = 0; t < 8; ++t)
+        pb[t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mc));
+      // row sum of the rounded probabilities actually multiplied with V
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            pb[t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[mt][half * 8 + t], c2, -mc));
-          // row sum of the rounded probabilities actually multiplied with V
-#pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            bf16x2 pr = {pb[t], pb[t + 1]};
-            l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
-          }
-          const int ks = mt * 2 + half;  // 16-key step inside the chunk
-          bf16x8 a[DT];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            a[dt] = *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi));
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt], pb, acc[dt], 0, 0, 0);
-        }
+      for (int t = 0; t < 8; t += 2) {
+        bf16x2 pr = {pb[t], pb[t + 1]};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
       }
+      const int ks = kb * 2 + half;  // 16-key step inside the chunk
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi)), pb,
+            acc[dt], 0, 0, 0);
     }
+  }
+
+  // One staged chunk with ck valid keys (1..64).
+  __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
+                                        int col, int hi) {
+    block32(lk, lvt, 0, min(ck, 32), c2, col, hi);
+    if (ck > 32) block32(lk, lvt, 1, ck - 32, c2, col, hi);
   }
 
   // Normalise and write this lane's query row (d channels, bf16) to op.
