@@ -82,7 +82,7 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m block_sparse_attention_tile_amd.build`")
-    L = C.CDLL(LIB_PATH)
+    L = C.CDLL(LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)  # unresolved symbols fail here
     P = C.c_void_p
     sz = C.c_size_t
     L.vsa_plan.argtypes = [C.POINTER(vsa_problem), C.POINTER(vsa_mask_policy), C.POINTER(P)]

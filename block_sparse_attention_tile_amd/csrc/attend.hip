@@ -104,8 +104,7 @@ struct ChunkIter {
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
 // Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
 // the lane's global source is picked so that LDS ends up in the swizzled
-// layout of Lds<D>.  Per-lane source offsets depend only on the lane and the
-// tile's slot count and are computed once.  Every wave issues exactly PER
+// layout of Lds<D>.  Every wave issues exactly PER
 // instructions per chunk (waves with fewer real pieces repeat their last
 // one), so a wait can count loads per chunk.  A 32-key chunk clamps the
 // source rows / key columns past 32 to the last valid ones: every access
@@ -116,39 +115,40 @@ struct ChunkLoader {
   static constexpr int VI = D / 8;         // V^T instructions
   static constexpr int NI = KI + VI;
   static constexpr int PER = (NI + NW - 1) / NW;
-  int off_full[PER];  // source element offsets, 64-key chunk
-  int off_half[PER];  // source element offsets, 32-key chunk
-  int dst[PER];       // LDS element offset inside a stage
+  int wave;   // wave-uniform
+  int lane;
+  int slots;
 
-  __device__ __forceinline__ void init(int wave, int lane, int slots) {
-#pragma unroll
-    for (int x = 0; x < PER; ++x) {
-      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
-      const int P = ins * 64 + lane;
-      dst[x] = ins * 512;
-      if (ins < KI) {
-        const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
-        const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
-        off_full[x] = r * D + c * 8;
-        off_half[x] = min(r, 31) * D + c * 8;
-      } else {
-        const int Pv = P - KI * 64;
-        const int d = Pv / 8, pc = Pv % 8;
-        const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
-        off_full[x] = d * slots + c * 8;
-        off_half[x] = d * slots + min(c, 3) * 8;
-      }
+  __device__ __forceinline__ void init(int w, int l, int sl) {
+    wave = __builtin_amdgcn_readfirstlane(w);
+    lane = l;
+    slots = sl;
+  }
+
+  // Source element offset (inside the chunk's tile data) and LDS element
+  // offset of this lane's 16-byte piece of instruction ins.  Swizzle
+  // arithmetic only (row widths are powers of two).
+  __device__ __forceinline__ int src_off(int ins, bool half) const {
+    const int P = ins * 64 + lane;
+    if (ins < KI) {
+      const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
+      const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
+      return (half ? min(r, 31) : r) * D + c * 8;
     }
+    const int Pv = P - KI * 64;
+    const int d = Pv / 8, pc = Pv % 8;
+    const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
+    return d * slots + (half ? min(c, 3) : c) * 8;
   }
 
   __device__ __forceinline__ void issue(uint16_t* stage, const uint16_t* __restrict__ kbase,
-                                        const uint16_t* __restrict__ vbase, bool half, int wave) const {
+                                        const uint16_t* __restrict__ vbase, bool half) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);
+      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
       const uint16_t* base = ins < KI ? kbase : vbase;
-      const int o = half ? off_half[x] : off_full[x];
-      __builtin_amdgcn_global_load_lds(base + o, (lds_ptr_t)(stage + dst[x]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + src_off(ins, half), (lds_ptr_t)(stage + ins * 512), 16,
+                                       0, 0);
     }
   }
 };
@@ -172,13 +172,13 @@ __device__ __forceinline__ void wait_chunk_and_barrier(int later) {
   }
 }
 
-template <int NW>
-struct Occ {
-  static constexpr int kWavesPerSimd = NW > 8 ? 3 : 2;
-};
+// Waves per SIMD the register budget is sized for: QT >= 2 waves hold QT
+// query tiles (up to 512 VGPRs, one wave per SIMD); 12-wave groups run 3 per
+// SIMD; the rest 2.
+constexpr int waves_per_simd(int nw, int qt) { return qt > 1 ? 1 : (nw > 8 ? 3 : 2); }
 
-template <int D, int NW, int STAGES>
-__global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel(
+template <int D, int NW, int STAGES, int QT>
+__global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel(
     Geo g, int blocking, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vt, const int* __restrict__ row_len, const int* __restrict__ col_idx,
     const int* __restrict__ cand, uint16_t* __restrict__ o, int nsb, int n_items) {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
   const BlkGeo b = pick_blk(g, blocking);
   if (i >= b.n_tiles) return;
   const int slots = b.slots;
-  const int q0 = sb * NW * 32;
+  const int q0 = sb * NW * 32 * QT;
   if (q0 >= slots) return;
 
   const int tid = threadIdx.x;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
   const int wave = tid >> 6;
   const int col = lane & 31;  // query column inside the wave's 32 rows
   const int hi = lane >> 5;   // wave half
-  const int qrow = q0 + wave * 32;
+  const int qrow = q0 + wave * 32 * QT;  // first query row of this wave
   const bool active = qrow < slots;
   const long head_tm = bh * g.tok_cap * D;
 
@@ -214,8 +214,11 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
   const int* gcols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
   for (int e = tid; e < L; e += NW * 64) cols[e] = gcols[e];
 
-  core::WaveState<D> ws;
-  if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
+  core::WaveState<D, QT> ws;
+  if (active) {
+    const uint16_t* qtile = qt + head_tm + (long)i * slots * D;
+    ws.init([&](int t) { return qtile + (long)min(qrow + 32 * t + col, slots - 1) * D; }, hi);
+  }
   const float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
   Loader ldr;
   ldr.init(wave, lane, slots);
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
   for (int s = 0; s < STAGES - 1; ++s) {
     if (s < total) {
       ldr.issue(lds + s * Lds<D>::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
-                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32, wave);
+                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
       ld_it.next(cols, L, g, b);
     }
   }
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
     if (nc < total) {
       ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
                 kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
-                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32, wave);
+                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
       ld_it.next(cols, L, g, b);
     }
     const uint16_t* lk = lds + (c % STAGES) * Lds<D>::STAGE;
@@ -256,29 +259,50 @@ __global__ __launch_bounds__(NW * 64, Occ<NW>::kWavesPerSimd) void attend_kernel
 
   if (!active) return;
   const TileInfo ti = tinfo(g, b, i);
-  const int qs = qrow + col;  // slot of this lane's query
-  const bool valid = qs < ti.nvalid;
-  uint16_t* op = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
-  ws.store(op, hi, valid);
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int qs = qrow + 32 * t + col;  // slot of this lane's query
+    const bool valid = qs < ti.nvalid;
+    uint16_t* op = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
+    ws.store(t, op, hi, valid);
+  }
 }
 
-template <int D, int NW, int STAGES>
+// Explicit instantiations of every kernel the launchers can pick.  (With
+// several implicit instantiations sharing a wave count, taking a kernel's
+// host-side address for hipFuncSetAttribute has left some host stubs
+// undefined in the shared library.)
+#define VSA_ATTEND_INST(D, NW, ST, QT)                                                              \
+  template __global__ void attend_kernel<D, NW, ST, QT>(Geo, int, const uint16_t*, const uint16_t*, \
+                                                        const uint16_t*, const int*, const int*,     \
+                                                        const int*, uint16_t*, int, int);
+#define VSA_ATTEND_INST_D(D)                                                               \
+  VSA_ATTEND_INST(D, 1, 2, 1) VSA_ATTEND_INST(D, 2, 2, 1) VSA_ATTEND_INST(D, 3, 2, 1)    \
+  VSA_ATTEND_INST(D, 4, 2, 1) VSA_ATTEND_INST(D, 5, 2, 1) VSA_ATTEND_INST(D, 6, 2, 1)    \
+  VSA_ATTEND_INST(D, 7, 2, 1) VSA_ATTEND_INST(D, 8, 2, 1) VSA_ATTEND_INST(D, 9, 4, 1)    \
+  VSA_ATTEND_INST(D, 10, 4, 1) VSA_ATTEND_INST(D, 11, 4, 1) VSA_ATTEND_INST(D, 12, 4, 1)
+VSA_ATTEND_INST_D(128)
+VSA_ATTEND_INST_D(64)
+#undef VSA_ATTEND_INST_D
+#undef VSA_ATTEND_INST
+
+template <int D, int NW, int STAGES, int QT = 1>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
-  const int nsb = (slabs + NW - 1) / NW;
+  const int nsb = (slabs + NW * QT - 1) / (NW * QT);
   const long items = (long)g.B * g.H * g.max_tiles * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
   const size_t shmem = (size_t)STAGES * Lds<D>::STAGE * sizeof(uint16_t) + (size_t)g.row_cap * 4;
   static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
   if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES, QT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES, QT>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, w.qt, w.kt, w.vt, w.row_len, w.col_idx, cand, o, nsb, (int)items);
   return hipGetLastError();
 }

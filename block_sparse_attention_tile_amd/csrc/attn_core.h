@@ -1,7 +1,7 @@
 // Per-wave flash-attention core shared by the tile and the fine-grained
 // attention kernels (CDNA4 / gfx950, v_mfma_f32_32x32x16_bf16).
 //
-// A wave owns 32 query rows.  For each chunk of up to 64 keys staged in LDS
+// A wave owns QT x 32 query rows.  For each chunk of up to 64 keys staged in LDS
 // (K by key rows, V transposed [d][key], both swizzled) it computes S^T = K Q^T, masks keys
 // past the chunk's valid count, updates the online softmax (running max and
 // sum; the result equals masked softmax attention, SPADE review page,
@@ -58,81 +58,109 @@ struct Lds {
   }
 };
 
-template <int D>
+// QT 32-query column tiles per wave: every K / V^T fragment read from LDS
+// feeds QT MFMAs, which divides the LDS read traffic per FLOP by QT.
+template <int D, int QT = 1>
 struct WaveState {
   static constexpr int DK = D / 16;  // MFMA k-steps over the head dimension
   static constexpr int DT = D / 32;  // 32-row blocks of O^T
-  bf16x8 qf[DK];                     // Q fragment (B operand: k = head dim, n = query)
-  f32x16 acc[DT];                    // O^T accumulators
-  float m_run;                       // running max (raw score units)
-  float l_part;                      // this lane half's partial row sum
+  bf16x8 qf[QT][DK];                 // Q fragments (B operand: k = head dim, n = query)
+  f32x16 acc[QT][DT];                // O^T accumulators
+  float m_run[QT];                   // running max (raw score units)
+  float l_part[QT];                  // this lane half's partial row sum
 
+  // q_ptr(qt) points at the query row of column tile qt owned by this lane.
+  template <class QPtr>
+  __device__ __forceinline__ void init(QPtr q_ptr, int hi) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const uint16_t* p = q_ptr(qt);
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) qf[qt][kk] = *reinterpret_cast<const bf16x8*>(p + kk * 16 + hi * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qt][dt][r] = 0.f;
+      m_run[qt] = -INFINITY;
+      l_part[qt] = 0.f;
+    }
+  }
   __device__ __forceinline__ void init(const uint16_t* qrow_ptr, int hi) {
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qrow_ptr + kk * 16 + hi * 8);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-    m_run = -INFINITY;
-    l_part = 0.f;
+    init([&](int qt) { return qrow_ptr + (long)qt * 32 * D; }, hi);
   }
 
   // One 32-key block (keys kb*32 .. kb*32+31 of the staged chunk), of which
   // the first nk are valid.  c2 = softmax scale * log2(e).
   __device__ __forceinline__ void block32(const uint16_t* lk, const uint16_t* lvt, int kb, int nk,
                                           float c2, int col, int hi) {
-    // S^T = K Q^T for 32 keys x 32 queries
+    // S^T = K Q^T for 32 keys x 32 queries, one query column tile at a time
+    // (K fragments read from LDS once and reused by every tile), followed
+    // directly by that tile's softmax so only one S tile is live.
     const int row = kb * 32 + key_perm(col);
-    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, hi)), qf[0], f32x16{}, 0, 0, 0);
+    bf16x8 ka[DK];
 #pragma unroll
-    for (int kk = 1; kk < DK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi)), qf[kk], s, 0, 0, 0);
-    // keys past the valid count (only in a tile's last block)
-    if (nk < 32) {
+    for (int kk = 0; kk < DK; ++kk)
+      ka[kk] = *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi));
+    bf16x8 pb[QT][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (16 * (r >> 3) + 8 * hi + (r & 7) >= nk) s[r] = -INFINITY;
+    for (int qt = 0; qt < QT; ++qt) {
+      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[qt][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < DK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[qt][kk], s, 0, 0, 0);
+      // keys past the valid count (only in a tile's last block)
+      if (nk < 32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + 8 * hi + (r & 7) >= nk) s[r] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      // Lazy rescaling: the running max (the same value in both lane halves
+      // of a query) is raised only when some score exceeds it by more than
+      // 2^8 in exp2 units, so every probability stays <= 256 and the final
+      // normalisation by the same running sum is exact.  The decision needs
+      // only each lane's own 16 keys and a wave vote; the exchange between
+      // the two halves happens only on the (rare) raise.
+      if (__any((mx - m_run[qt]) * c2 > 8.0f)) {
+        const float m_new = fmaxf(m_run[qt], fmaxf(mx, __shfl_xor(mx, 32)));
+        const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
+        l_part[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qt][dt][r] *= alpha;
+        m_run[qt] = m_new;
+      }
+      const float mc = m_run[qt] * c2;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          pb[qt][half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mc));
+        // row sum of the rounded probabilities actually multiplied with V
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          bf16x2 pr = {pb[qt][half][t], pb[qt][half][t + 1]};
+          l_part[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part[qt], false);
+        }
+      }
+      // keep the scheduler from overlapping several tiles' S (register bound)
+      if (QT > 1) __builtin_amdgcn_sched_barrier(0);
     }
-    float mx = s[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: raise the running max only when a score exceeds it by
-    // more than 2^8 in exp2 units; probabilities stay <= 256 and the final
-    // normalisation by the same running sum is exact.
-    const float m_new = fmaxf(m_run, mx);
-    if (__any((m_new - m_run) * c2 > 8.0f)) {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_part *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = m_run * c2;
+    // O^T += V^T P^T
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      bf16x8 pb;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        pb[t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mc));
-      // row sum of the rounded probabilities actually multiplied with V
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        bf16x2 pr = {pb[t], pb[t + 1]};
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
-      }
       const int ks = kb * 2 + half;  // 16-key step inside the chunk
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi)), pb,
-            acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt][half], acc[qt][dt], 0, 0, 0);
+      }
     }
   }
 
@@ -143,10 +171,10 @@ struct WaveState {
     if (ck > 32) block32(lk, lvt, 1, ck - 32, c2, col, hi);
   }
 
-  // Normalise and write this lane's query row (d channels, bf16) to op.
-  // Must be called by both lane halves (they exchange their partial sums).
-  __device__ __forceinline__ void store(uint16_t* op, int hi, bool write) {
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
+  // Normalise and write the query row of column tile qt (d channels, bf16)
+  // to op.  Both lane halves must call it (they exchange partial sums).
+  __device__ __forceinline__ void store(int qt, uint16_t* op, int hi, bool write) {
+    const float l_tot = l_part[qt] + __shfl_xor(l_part[qt], 32);
     if (!write) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -156,7 +184,7 @@ struct WaveState {
         const int d0 = dt * 32 + 8 * r4 + 4 * hi;
         __bf16 h[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[dt][4 * r4 + x] * inv);
+        for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[qt][dt][4 * r4 + x] * inv);
         uint2 pk;
         pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
@@ -166,6 +194,7 @@ struct WaveState {
       }
     }
   }
+  __device__ __forceinline__ void store(uint16_t* op, int hi, bool write) { store(0, op, hi, write); }
 };
 
 }  // namespace core

@@ -30,6 +30,12 @@ def test_library_exports_every_declared_function():
     assert sorted(_lib.EXPORTED) == declared
 
 
+def test_library_has_no_unresolved_symbols():
+    # RTLD_NOW resolves every symbol at load time (a missing kernel stub
+    # would otherwise surface only when its launcher runs)
+    ctypes.CDLL(_lib.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_status_strings():
     L = vsa.lib()
     assert L.vsa_status_string(0) == b"VSA_OK"
