@@ -25,7 +25,8 @@ METRIC = ("ms/attention call + effective TFLOP/s on retained blocks, "
           "HunyuanVideo-720p shape")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ATTN_SOURCES = ["block_sparse_attention_tile_amd/csrc/attend.hip"]
+ATTN_SOURCES = ["block_sparse_attention_tile_amd/csrc/attend.hip",
+                "block_sparse_attention_tile_amd/csrc/attn_core.h"]
 
 
 def _src_hash(paths):
