@@ -173,7 +173,9 @@ def main():
     ms_attend = stage(lambda: plan.attend(o, q, k, v), n_st)
 
     BH = wl.B * wl.H
-    bytes_layout = 6.0 * BH * wl.N * wl.d * 2          # read Q,K,V + write tile-major copies
+    # read Q, K, V + write the tile-major copies (no layout stage for the
+    # fine-grained mask, which reads the raster tensors directly)
+    bytes_layout = 0.0 if wl.fine_group else 6.0 * BH * wl.N * wl.d * 2
     attn_tflops = flops / (ms_attend * 1e-3) / 1e12
     traffic = _traffic("attend", wl.name)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -181,7 +183,7 @@ def main():
                 "traffic": traffic}
 
     cpu = None
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and not wl.fine_group and not wl.candidates:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = _cpu_baseline(wl, q, k, v, plan, args.cpu_budget)
 
@@ -206,8 +208,9 @@ def main():
                    "retained_flops": flops, "parallelism": "single GPU"},
         "stages_ms": {"layout": round(ms_layout, 4), "select": round(ms_select, 4),
                       "attend": round(ms_attend, 4)},
-        "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1),
-        "layout_hbm_frac": round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1) if bytes_layout else None,
+        "layout_hbm_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                            if bytes_layout else None),
         "attend_tflops": round(attn_tflops, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
