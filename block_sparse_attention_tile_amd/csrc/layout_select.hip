@@ -60,16 +60,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // One workgroup per (head, tile): copies Q and K rows to tile-major order,
 // writes V transposed per tile ([d][slots]) through LDS, and optionally the
 // exact per-tile means of Q and K (fp64 sums of bf16 values, one rounding).
+// The Q/K copy runs first with no barrier in it (four rows per thread in
+// flight); only the V transpose is staged through LDS.
 template <int D>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ qt, uint16_t* __restrict__ kt,
     uint16_t* __restrict__ vt, float* __restrict__ pooled_q, float* __restrict__ pooled_k,
     const int* __restrict__ cand, int pool) {
-  constexpr int P = D / 8;                    // 16-byte pieces per row
-  constexpr int RPP = kLayoutThreads / P;     // rows per pass
-  __shared__ uint32_t lv[kChunk][D / 2 + 1];  // V chunk, odd row stride: no bank conflicts
-  __shared__ double red[kLayoutThreads][8];
+  constexpr int P = D / 8;                       // 16-byte pieces per row
+  constexpr int RPP = kLayoutThreads / P;        // rows per pass
+  constexpr int LVW = D / 2 + 1;                 // V chunk row stride in words (odd: no bank conflicts)
+  constexpr int kWords = kChunk * LVW > kLayoutThreads * 16 ? kChunk * LVW : kLayoutThreads * 16;
+  __shared__ uint32_t smem[kWords];              // V chunk; reused for the pooled-sum reduction
+  constexpr int U = 4;                           // rows per thread in flight (Q/K copy)
 
   const int i = blockIdx.x;
   const long bh = blockIdx.y;
@@ -87,23 +91,30 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
 #pragma unroll
   for (int x = 0; x < 8; ++x) sq[x] = sk[x] = 0.0;
 
-  for (int s0 = 0; s0 < b.slots; s0 += kChunk) {
-    for (int rr = r0; rr < kChunk; rr += RPP) {
-      const int s = s0 + rr;
-      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
+  // Q and K: gather raster rows, store contiguous tile-major rows.
+  for (int s0 = r0; s0 < b.slots; s0 += RPP * U) {
+    uint4 qv[U], kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * RPP;
+      qv[u] = make_uint4(0, 0, 0, 0);
+      kv[u] = qv[u];
       if (s < t.nvalid) {
         const long off = in_base + token_of(g, b, t, s) * D + p * 8;
-        qv = *reinterpret_cast<const uint4*>(q + off);
-        kv = *reinterpret_cast<const uint4*>(k + off);
-        vv = *reinterpret_cast<const uint4*>(v + off);
+        qv[u] = *reinterpret_cast<const uint4*>(q + off);
+        kv[u] = *reinterpret_cast<const uint4*>(k + off);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * RPP;
       if (s < b.slots) {
-        *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv;
-        *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv;
+        *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv[u];
+        *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv[u];
       }
       if (pool) {
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        const uint32_t qw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+        const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           sq[2 * x] += (double)bf16_lo(qw[x]);
@@ -112,15 +123,31 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
           sk[2 * x + 1] += (double)bf16_hi(kw[x]);
         }
       }
-      lv[rr][p * 4 + 0] = vv.x;
-      lv[rr][p * 4 + 1] = vv.y;
-      lv[rr][p * 4 + 2] = vv.z;
-      lv[rr][p * 4 + 3] = vv.w;
+    }
+  }
+
+  // V: chunks of 64 slots through LDS, written transposed ([d][slots]).
+  const long vt_base = bh * g.tok_cap * D + (long)i * D * b.slots;
+  for (int s0 = 0; s0 < b.slots; s0 += kChunk) {
+    uint4 vv[kChunk / RPP];
+#pragma unroll
+    for (int u = 0; u < kChunk / RPP; ++u) {
+      const int s = s0 + r0 + u * RPP;
+      vv[u] = make_uint4(0, 0, 0, 0);
+      if (s < t.nvalid)
+        vv[u] = *reinterpret_cast<const uint4*>(v + in_base + token_of(g, b, t, s) * D + p * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk / RPP; ++u) {
+      uint32_t* row = smem + (r0 + u * RPP) * LVW + p * 4;
+      row[0] = vv[u].x;
+      row[1] = vv[u].y;
+      row[2] = vv[u].z;
+      row[3] = vv[u].w;
     }
     __syncthreads();
     // V^T pieces: 8 consecutive slots of one channel row; 8 lanes cover a
     // 128-byte run of the row.
-    const long vt_base = bh * g.tok_cap * D + (long)i * D * b.slots;
     for (int pc = tid; pc < D * (kChunk / 8); pc += kLayoutThreads) {
       const int s8 = pc % (kChunk / 8);
       const int dd = pc / (kChunk / 8);
@@ -129,7 +156,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
       uint32_t h[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t wv = lv[s8 * 8 + j][dd >> 1];
+        const uint32_t wv = smem[(s8 * 8 + j) * LVW + (dd >> 1)];
         h[j] = (dd & 1) ? (wv >> 16) : (wv & 0xffffu);
       }
       uint4 out;
@@ -145,14 +172,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
   if (!pool) return;
   // Exact sums: every partial sum of bf16 values of moderate range is exact
   // in fp64, so the reduction order does not change the result.
+  double* red = reinterpret_cast<double*>(smem);  // [kLayoutThreads][8]
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) red[tid][x] = which ? sk[x] : sq[x];
+    for (int x = 0; x < 8; ++x) red[tid * 8 + x] = which ? sk[x] : sq[x];
     __syncthreads();
     if (tid < D) {
       const int pp = tid / 8, xx = tid % 8;
       double s = 0.0;
-      for (int r = 0; r < RPP; ++r) s += red[r * P + pp][xx];
+      for (int r = 0; r < RPP; ++r) s += red[(r * P + pp) * 8 + xx];
       float* dst = which ? pooled_k : pooled_q;
       dst[(bh * g.max_tiles + i) * D + tid] = (float)(s / (double)t.nvalid);
     }
