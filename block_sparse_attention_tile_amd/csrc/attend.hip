@@ -14,9 +14,8 @@
 //    crosses from L2 into LDS once per query tile.  A wave owns 32 query rows
 //    for the whole KV sweep; its Q fragment stays in VGPRs.
 //  * K and V^T stream in chunks of 64 (or a final 32) keys through a ring of
-//    LDS stages filled by direct global->LDS loads (no VGPR staging); up to
-//    STAGES-1 chunks are in flight while one is multiplied, and the wait for
-//    a chunk counts only the loads issued before it (s_waitcnt vmcnt(n)).
+//    LDS stages filled by direct global->LDS loads (no VGPR staging); half of
+//    the ring is multiplied per barrier while the other half is in flight.
 //  * The kept-tile list is copied to LDS first, so the loop issues no other
 //    global loads that would drain the queue.
 //  * The MFMA / online-softmax math per 32-key block is in attn_core.h.
@@ -85,7 +84,7 @@ struct ChunkIter {
   __device__ __forceinline__ void start(const int* cols, int L, const Geo& g, const BlkGeo& b) {
     e = 0;
     off = 0;
-    j = L > 0 ? cols[0] : 0;
+    j = L > 0 ? __builtin_amdgcn_readfirstlane(cols[0]) : 0;
     nv = L > 0 ? tile_nvalid(g, b, j) : 0;
   }
   __device__ __forceinline__ void next(const int* cols, int L, const Geo& g, const BlkGeo& b) {
@@ -93,7 +92,7 @@ struct ChunkIter {
     if (off >= nv) {
       off = 0;
       if (++e < L) {
-        j = cols[e];
+        j = __builtin_amdgcn_readfirstlane(cols[e]);  // uniform: keep the iterator scalar
         nv = tile_nvalid(g, b, j);
       }
     }
@@ -115,40 +114,43 @@ struct ChunkLoader {
   static constexpr int VI = D / 8;         // V^T instructions
   static constexpr int NI = KI + VI;
   static constexpr int PER = (NI + NW - 1) / NW;
-  int wave;   // wave-uniform
-  int lane;
-  int slots;
+  int wave;           // wave-uniform
+  int off_full[PER];  // source element offsets of this lane's pieces, 64-key chunk
+  int off_half[PER];  // the same for a 32-key chunk
 
-  __device__ __forceinline__ void init(int w, int l, int sl) {
-    wave = __builtin_amdgcn_readfirstlane(w);
-    lane = l;
-    slots = sl;
+  __device__ __forceinline__ static int ins_of(int wave, int x) {
+    return min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
   }
 
-  // Source element offset (inside the chunk's tile data) and LDS element
-  // offset of this lane's 16-byte piece of instruction ins.  Swizzle
-  // arithmetic only (row widths are powers of two).
-  __device__ __forceinline__ int src_off(int ins, bool half) const {
-    const int P = ins * 64 + lane;
-    if (ins < KI) {
-      const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
-      const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
-      return (half ? min(r, 31) : r) * D + c * 8;
+  __device__ __forceinline__ void init(int w, int lane, int slots) {
+    wave = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int ins = ins_of(wave, x);
+      const int P = ins * 64 + lane;
+      if (ins < KI) {
+        const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
+        const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
+        off_full[x] = r * D + c * 8;
+        off_half[x] = min(r, 31) * D + c * 8;
+      } else {
+        const int Pv = P - KI * 64;
+        const int d = Pv / 8, pc = Pv % 8;
+        const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
+        off_full[x] = d * slots + c * 8;
+        off_half[x] = d * slots + min(c, 3) * 8;
+      }
     }
-    const int Pv = P - KI * 64;
-    const int d = Pv / 8, pc = Pv % 8;
-    const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
-    return d * slots + (half ? min(c, 3) : c) * 8;
   }
 
   __device__ __forceinline__ void issue(uint16_t* stage, const uint16_t* __restrict__ kbase,
                                         const uint16_t* __restrict__ vbase, bool half) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-      const int ins = min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
+      const int ins = ins_of(wave, x);
       const uint16_t* base = ins < KI ? kbase : vbase;
-      __builtin_amdgcn_global_load_lds(base + src_off(ins, half), (lds_ptr_t)(stage + ins * 512), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(base + (half ? off_half[x] : off_full[x]),
+                                       (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
     }
   }
 };
@@ -173,9 +175,10 @@ __device__ __forceinline__ void wait_chunk_and_barrier(int later) {
 }
 
 // Waves per SIMD the register budget is sized for: QT >= 2 waves hold QT
-// query tiles (up to 512 VGPRs, one wave per SIMD); 12-wave groups run 3 per
-// SIMD; the rest 2.
-constexpr int waves_per_simd(int nw, int qt) { return qt > 1 ? 1 : (nw > 8 ? 3 : 2); }
+// query tiles (up to 512 VGPRs, one wave per SIMD); one- and two-wave groups
+// (whose loaders keep many per-lane offsets) get 2; all others 3 (168 VGPRs),
+// so two small workgroups can share a CU.
+constexpr int waves_per_simd(int nw, int qt) { return qt > 1 ? 1 : (nw > 2 ? 3 : 2); }
 
 template <int D, int NW, int STAGES, int QT>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel(
@@ -233,28 +236,41 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
   ChunkIter ld_it, cur;
   ld_it.start(cols, L, g, b);
   cur = ld_it;
-  // prologue: chunks 0 .. STAGES-2
+  // The ring holds STAGES chunks in two halves of CPB = STAGES/2 chunks.  The
+  // prologue loads the first half; each iteration waits for the half it is
+  // about to multiply (everything issued so far), refills the other half
+  // (freed by the previous iteration) and multiplies CPB chunks: one barrier
+  // per CPB chunks, CPB chunks always in flight.
+  constexpr int CPB = STAGES / 2;
+  static_assert(STAGES >= 2 && STAGES % 2 == 0, "stages come in pairs");
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
+  for (int s = 0; s < CPB; ++s) {
     if (s < total) {
       ldr.issue(lds + s * Lds<D>::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                 vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
       ld_it.next(cols, L, g, b);
     }
   }
-  for (int c = 0; c < total; ++c) {
-    // chunk c's loads are done once only the later-issued ones are pending
-    wait_chunk_and_barrier<Loader::PER>(min(STAGES - 2, total - 1 - c));
-    const int nc = c + STAGES - 1;  // refill the stage freed by chunk c-1
-    if (nc < total) {
-      ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
-                kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
-                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-      ld_it.next(cols, L, g, b);
+  for (int c = 0; c < total; c += CPB) {
+    wait_chunk_and_barrier<Loader::PER>(0);
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      const int nc = c + CPB + u;
+      if (nc < total) {
+        ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
+                  kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+                  vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
+        ld_it.next(cols, L, g, b);
+      }
     }
-    const uint16_t* lk = lds + (c % STAGES) * Lds<D>::STAGE;
-    if (active) ws.chunk(lk, lk + Lds<D>::KE, cur.keys(), c2, col, hi);
-    cur.next(cols, L, g, b);
+#pragma unroll
+    for (int u = 0; u < CPB; ++u) {
+      if (c + u < total) {
+        const uint16_t* lk = lds + ((c + u) % STAGES) * Lds<D>::STAGE;
+        if (active) ws.chunk(lk, lk + Lds<D>::KE, cur.keys(), c2, col, hi);
+        cur.next(cols, L, g, b);
+      }
+    }
   }
 
   if (!active) return;
