@@ -103,9 +103,8 @@ struct ChunkIter {
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
 // Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
 // the lane's global source is picked so that LDS ends up in the swizzled
-// layout of Lds<D>.  Every wave issues exactly PER
-// instructions per chunk (waves with fewer real pieces repeat their last
-// one), so a wait can count loads per chunk.  A 32-key chunk clamps the
+// layout of Lds<D>.  The NI instructions of a chunk are dealt round-robin
+// over the waves.  A 32-key chunk clamps the
 // source rows / key columns past 32 to the last valid ones: every access
 // stays inside the tile and the extra LDS slots are never read.
 template <int D, int NW>
@@ -119,7 +118,7 @@ struct ChunkLoader {
   int off_half[PER];  // the same for a 32-key chunk
 
   __device__ __forceinline__ static int ins_of(int wave, int x) {
-    return min(wave + x * NW, wave + ((NI - 1 - wave) / NW) * NW);  // repeat the last
+    return min(wave + x * NW, NI - 1);  // past the last: clamped, never issued
   }
 
   __device__ __forceinline__ void init(int w, int lane, int slots) {
@@ -147,6 +146,7 @@ struct ChunkLoader {
                                         const uint16_t* __restrict__ vbase, bool half) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
+      if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
       const uint16_t* base = ins < KI ? kbase : vbase;
       __builtin_amdgcn_global_load_lds(base + (half ? off_half[x] : off_full[x]),
@@ -155,23 +155,11 @@ struct ChunkLoader {
   }
 };
 
-// Wait until at most `later` chunks' loads (PER instructions each) of this
-// wave are outstanding, then barrier.  The count is a small run-time value;
-// s_waitcnt takes an immediate, hence the switch.
-template <int PER>
-__device__ __forceinline__ void wait_chunk_and_barrier(int later) {
-  switch (later * PER) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
-#define VSA_WAIT_CASE(n) \
-  case n: asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory"); break;
-    VSA_WAIT_CASE(1) VSA_WAIT_CASE(2) VSA_WAIT_CASE(3) VSA_WAIT_CASE(4) VSA_WAIT_CASE(5)
-    VSA_WAIT_CASE(6) VSA_WAIT_CASE(7) VSA_WAIT_CASE(8) VSA_WAIT_CASE(9) VSA_WAIT_CASE(10)
-    VSA_WAIT_CASE(12) VSA_WAIT_CASE(14) VSA_WAIT_CASE(15) VSA_WAIT_CASE(16) VSA_WAIT_CASE(18)
-    VSA_WAIT_CASE(20) VSA_WAIT_CASE(21) VSA_WAIT_CASE(24) VSA_WAIT_CASE(28) VSA_WAIT_CASE(30)
-    VSA_WAIT_CASE(32) VSA_WAIT_CASE(36) VSA_WAIT_CASE(40) VSA_WAIT_CASE(42) VSA_WAIT_CASE(48)
-#undef VSA_WAIT_CASE
-    default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
-  }
+// All of this wave's outstanding loads have landed, then barrier: after it
+// every wave's pieces of the chunks issued so far are visible in LDS, and
+// every wave is done with the stages the next loads will overwrite.
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Waves per SIMD the register budget is sized for: QT >= 2 waves hold QT
@@ -252,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
     }
   }
   for (int c = 0; c < total; c += CPB) {
-    wait_chunk_and_barrier<Loader::PER>(0);
+    wait_loads_and_barrier();
 #pragma unroll
     for (int u = 0; u < CPB; ++u) {
       const int nc = c + CPB + u;
