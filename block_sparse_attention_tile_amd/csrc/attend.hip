@@ -74,27 +74,34 @@ __device__ __forceinline__ long token_of(const Geo& g, const BlkGeo& b, const Ti
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Iterator over the 64-key chunks of a query tile's kept key tiles (read
-// from the LDS copy of the list).
+// The kept-tile list in LDS holds, per entry, the key tile j in the low
+// kTileBits bits and its valid key count above them (tiles are limited to
+// 4096 of at most 4096 tokens), so the chunk iterators never divide.
+constexpr int kTileBits = 13;
+
+// Iterator over the 64-key chunks of a query tile's kept key tiles.
 struct ChunkIter {
   int e;    // position in the kept list
   int j;    // key tile
   int off;  // first slot of the chunk inside tile j
   int nv;   // valid keys of tile j
-  __device__ __forceinline__ void start(const int* cols, int L, const Geo& g, const BlkGeo& b) {
+  __device__ __forceinline__ void load(const int* cols) {
+    const int x = __builtin_amdgcn_readfirstlane(cols[e]);  // uniform: keep the iterator scalar
+    j = x & ((1 << kTileBits) - 1);
+    nv = x >> kTileBits;
+  }
+  __device__ __forceinline__ void start(const int* cols, int L) {
     e = 0;
     off = 0;
-    j = L > 0 ? __builtin_amdgcn_readfirstlane(cols[0]) : 0;
-    nv = L > 0 ? tile_nvalid(g, b, j) : 0;
+    j = 0;
+    nv = 0;
+    if (L > 0) load(cols);
   }
-  __device__ __forceinline__ void next(const int* cols, int L, const Geo& g, const BlkGeo& b) {
+  __device__ __forceinline__ void next(const int* cols, int L) {
     off += kKC;
     if (off >= nv) {
       off = 0;
-      if (++e < L) {
-        j = __builtin_amdgcn_readfirstlane(cols[e]);  // uniform: keep the iterator scalar
-        nv = tile_nvalid(g, b, j);
-      }
+      if (++e < L) load(cols);
     }
   }
   __device__ __forceinline__ int keys() const { return min(kKC, nv - off); }
@@ -102,17 +109,21 @@ struct ChunkIter {
 
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
 // Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
-// the lane's global source is picked so that LDS ends up in the swizzled
-// layout of Lds<D>.  The NI instructions of a chunk are dealt round-robin
-// over the waves.  A 32-key chunk clamps the
-// source rows / key columns past 32 to the last valid ones: every access
-// stays inside the tile and the extra LDS slots are never read.
+// the lane's global source is picked so that LDS ends up in the padded,
+// lane-ordered layout of Lds<D> (a padding unit re-reads its row's last data
+// unit).  The NI instructions of a chunk are dealt round-robin over the
+// waves.  A 32-key chunk clamps the source rows / key columns past 32 to the
+// last valid ones: every access stays inside the tile and the extra LDS slots
+// are never read.
 template <int D, int NW>
 struct ChunkLoader {
-  static constexpr int KI = Lds<D>::KC16;  // K instructions (1 KB each)
-  static constexpr int VI = D / 8;         // V^T instructions
+  static constexpr int KU = kKC * (Lds<D>::KC16 + 1);  // 16-byte units of the K part
+  static constexpr int VU = D * (Lds<D>::VC16 + 1);    // and of the V^T part
+  static constexpr int KI = KU / 64;                   // K instructions (1 KB each)
+  static constexpr int VI = VU / 64;                   // V^T instructions
   static constexpr int NI = KI + VI;
   static constexpr int PER = (NI + NW - 1) / NW;
+  static_assert(KU % 64 == 0 && VU % 64 == 0, "whole instructions per part");
   int wave;           // wave-uniform
   int off_full[PER];  // source element offsets of this lane's pieces, 64-key chunk
   int off_half[PER];  // the same for a 32-key chunk
@@ -126,16 +137,17 @@ struct ChunkLoader {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int ins = ins_of(wave, x);
-      const int P = ins * 64 + lane;
+      const int u = ins * 64 + lane;
       if (ins < KI) {
-        const int r = P / Lds<D>::KC16, pc = P % Lds<D>::KC16;
-        const int c = pc ^ (core::key_perm(r & 31) & (Lds<D>::KC16 - 1));
-        off_full[x] = r * D + c * 8;
-        off_half[x] = min(r, 31) * D + c * 8;
+        const int p = u / (Lds<D>::KC16 + 1);                   // physical row
+        const int c = min(u % (Lds<D>::KC16 + 1), Lds<D>::KC16 - 1);
+        const int key = (p & ~31) | core::key_perm(p & 31);
+        off_full[x] = key * D + c * 8;
+        off_half[x] = min(key, 31) * D + c * 8;
       } else {
-        const int Pv = P - KI * 64;
-        const int d = Pv / 8, pc = Pv % 8;
-        const int c = pc ^ ((d & 7) ^ ((d >> 3) & 1));
+        const int v = u - KU;
+        const int d = v / (Lds<D>::VC16 + 1);
+        const int c = min(v % (Lds<D>::VC16 + 1), Lds<D>::VC16 - 1);
         off_full[x] = d * slots + c * 8;
         off_half[x] = d * slots + min(c, 3) * 8;
       }
@@ -162,14 +174,13 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Waves per SIMD the register budget is sized for: QT >= 2 waves hold QT
-// query tiles (up to 512 VGPRs, one wave per SIMD); one- and two-wave groups
+// Waves per SIMD the register budget is sized for: one- and two-wave groups
 // (whose loaders keep many per-lane offsets) get 2; all others 3 (168 VGPRs),
 // so two small workgroups can share a CU.
-constexpr int waves_per_simd(int nw, int qt) { return qt > 1 ? 1 : (nw > 2 ? 3 : 2); }
+constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
-template <int D, int NW, int STAGES, int QT>
-__global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel(
+template <int D, int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     Geo g, int blocking, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vt, const int* __restrict__ row_len, const int* __restrict__ col_idx,
     const int* __restrict__ cand, uint16_t* __restrict__ o, int nsb, int n_items) {
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
   const BlkGeo b = pick_blk(g, blocking);
   if (i >= b.n_tiles) return;
   const int slots = b.slots;
-  const int q0 = sb * NW * 32 * QT;
+  const int q0 = sb * NW * 32;
   if (q0 >= slots) return;
 
   const int tid = threadIdx.x;
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
   const int wave = tid >> 6;
   const int col = lane & 31;  // query column inside the wave's 32 rows
   const int hi = lane >> 5;   // wave half
-  const int qrow = q0 + wave * 32 * QT;  // first query row of this wave
+  const int qrow = q0 + wave * 32;  // first query row of this wave
   const bool active = qrow < slots;
   const long head_tm = bh * g.tok_cap * D;
 
@@ -203,26 +214,29 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
   int* cols = reinterpret_cast<int*>(lds + STAGES * Lds<D>::STAGE);
   const int L = row_len[bh * g.max_tiles + i];
   const int* gcols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
-  for (int e = tid; e < L; e += NW * 64) cols[e] = gcols[e];
-
-  core::WaveState<D, QT> ws;
-  if (active) {
-    const uint16_t* qtile = qt + head_tm + (long)i * slots * D;
-    ws.init([&](int t) { return qtile + (long)min(qrow + 32 * t + col, slots - 1) * D; }, hi);
+  for (int e = tid; e < L; e += NW * 64) {
+    const int j = gcols[e];
+    cols[e] = (tile_nvalid(g, b, j) << kTileBits) | j;
   }
+
+  core::WaveState<D> ws;
+  if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
   Loader ldr;
   ldr.init(wave, lane, slots);
   __syncthreads();  // cols visible
 
-  // total chunks of the row
+  // total chunks of the row (each wave sums the list on its own)
   int total = 0;
-  for (int e = 0; e < L; ++e) total += (tile_nvalid(g, b, cols[e]) + kKC - 1) / kKC;
+  for (int e = lane; e < L; e += 64) total += ((cols[e] >> kTileBits) + kKC - 1) / kKC;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) total += __shfl_xor(total, m);
+  total = __builtin_amdgcn_readfirstlane(total);
 
   const uint16_t* kt_head = kt + head_tm;
   const uint16_t* vt_head = vt + head_tm;
   ChunkIter ld_it, cur;
-  ld_it.start(cols, L, g, b);
+  ld_it.start(cols, L);
   cur = ld_it;
   // The ring holds STAGES chunks in two halves of CPB = STAGES/2 chunks.  The
   // prologue loads the first half; each iteration waits for the half it is
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
     if (s < total) {
       ldr.issue(lds + s * Lds<D>::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                 vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-      ld_it.next(cols, L, g, b);
+      ld_it.next(cols, L);
     }
   }
   for (int c = 0; c < total; c += CPB) {
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
         ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
                   kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                   vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-        ld_it.next(cols, L, g, b);
+        ld_it.next(cols, L);
       }
     }
 #pragma unroll
@@ -256,57 +270,53 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW, QT)) void attend_kernel
       if (c + u < total) {
         const uint16_t* lk = lds + ((c + u) % STAGES) * Lds<D>::STAGE;
         if (active) ws.chunk(lk, lk + Lds<D>::KE, cur.keys(), c2, col, hi);
-        cur.next(cols, L, g, b);
+        cur.next(cols, L);
       }
     }
   }
 
   if (!active) return;
   const TileInfo ti = tinfo(g, b, i);
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    const int qs = qrow + 32 * t + col;  // slot of this lane's query
-    const bool valid = qs < ti.nvalid;
-    uint16_t* op = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
-    ws.store(t, op, hi, valid);
-  }
+  const int qs = qrow + col;  // slot of this lane's query
+  const bool valid = qs < ti.nvalid;
+  ws.store(o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D, hi, valid);
 }
 
 // Explicit instantiations of every kernel the launchers can pick.  (With
 // several implicit instantiations sharing a wave count, taking a kernel's
 // host-side address for hipFuncSetAttribute has left some host stubs
 // undefined in the shared library.)
-#define VSA_ATTEND_INST(D, NW, ST, QT)                                                              \
-  template __global__ void attend_kernel<D, NW, ST, QT>(Geo, int, const uint16_t*, const uint16_t*, \
-                                                        const uint16_t*, const int*, const int*,     \
-                                                        const int*, uint16_t*, int, int);
+#define VSA_ATTEND_INST(D, NW, ST)                                                                   \
+  template __global__ void attend_kernel<D, NW, ST>(Geo, int, const uint16_t*, const uint16_t*,     \
+                                                    const uint16_t*, const int*, const int*,         \
+                                                    const int*, uint16_t*, int, int);
 #define VSA_ATTEND_INST_D(D)                                                               \
-  VSA_ATTEND_INST(D, 1, 2, 1) VSA_ATTEND_INST(D, 2, 2, 1) VSA_ATTEND_INST(D, 3, 2, 1)    \
-  VSA_ATTEND_INST(D, 4, 2, 1) VSA_ATTEND_INST(D, 5, 2, 1) VSA_ATTEND_INST(D, 6, 2, 1)    \
-  VSA_ATTEND_INST(D, 7, 2, 1) VSA_ATTEND_INST(D, 8, 2, 1) VSA_ATTEND_INST(D, 9, 4, 1)    \
-  VSA_ATTEND_INST(D, 10, 4, 1) VSA_ATTEND_INST(D, 11, 4, 1) VSA_ATTEND_INST(D, 12, 4, 1)
+  VSA_ATTEND_INST(D, 1, 2) VSA_ATTEND_INST(D, 2, 2) VSA_ATTEND_INST(D, 3, 2)    \
+  VSA_ATTEND_INST(D, 4, 2) VSA_ATTEND_INST(D, 5, 2) VSA_ATTEND_INST(D, 6, 2)    \
+  VSA_ATTEND_INST(D, 7, 2) VSA_ATTEND_INST(D, 8, 2) VSA_ATTEND_INST(D, 9, 4)    \
+  VSA_ATTEND_INST(D, 10, 4) VSA_ATTEND_INST(D, 11, 4) VSA_ATTEND_INST(D, 12, 4)
 VSA_ATTEND_INST_D(128)
 VSA_ATTEND_INST_D(64)
 #undef VSA_ATTEND_INST_D
 #undef VSA_ATTEND_INST
 
-template <int D, int NW, int STAGES, int QT = 1>
+template <int D, int NW, int STAGES>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
-  const int nsb = (slabs + NW * QT - 1) / (NW * QT);
+  const int nsb = (slabs + NW - 1) / NW;
   const long items = (long)g.B * g.H * g.max_tiles * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
   const size_t shmem = (size_t)STAGES * Lds<D>::STAGE * sizeof(uint16_t) + (size_t)g.row_cap * 4;
   static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
   if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES, QT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES, QT>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, w.qt, w.kt, w.vt, w.row_len, w.col_idx, cand, o, nsb, (int)items);
   return hipGetLastError();
 }

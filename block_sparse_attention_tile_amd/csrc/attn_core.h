@@ -1,10 +1,10 @@
 // Per-wave flash-attention core shared by the tile and the fine-grained
 // attention kernels (CDNA4 / gfx950, v_mfma_f32_32x32x16_bf16).
 //
-// A wave owns QT x 32 query rows.  For each chunk of up to 64 keys staged in LDS
-// (K by key rows, V transposed [d][key], both swizzled) it computes S^T = K Q^T, masks keys
-// past the chunk's valid count, updates the online softmax (running max and
-// sum; the result equals masked softmax attention, SPADE review page,
+// A wave owns 32 query rows.  For each chunk of up to 64 keys staged in LDS
+// (K by key rows, V transposed [d][key]) it computes S^T = K Q^T, masks keys
+// past the chunk's valid count, updates the online softmax (running offset
+// and sum; the result equals masked softmax attention, SPADE review page,
 // ledger axiom on FlashAttention-style online softmax) and accumulates
 // O^T += V^T P^T.
 //
@@ -35,146 +35,178 @@ __device__ __forceinline__ int key_perm(int m) {
 }
 
 
-// LDS stage: K chunk [64 keys][D] and V^T chunk [D][64 keys], bf16, rows
-// unpadded so that a wave's 64 x 16-byte direct global->LDS load fills 1 KB
-// contiguously.  Bank conflicts of the 16-byte fragment reads are avoided by
-// XOR-swizzling the 16-byte column index with a function of the row chosen
-// so that any 8 (and any 16) consecutive lanes of a fragment read touch
-// distinct bank groups.
+// LDS stage: K chunk [64 keys][D] and V^T chunk [D][64 keys], bf16.  Every
+// row is padded by one 16-byte unit, so that consecutive rows start in
+// consecutive 16-byte bank groups: the 16-byte fragment reads of 8 (and of
+// 16) consecutive lanes, which read consecutive rows at one column, touch
+// distinct banks, and every fragment a lane reads sits at a compile-time
+// offset from one per-lane base address.  K rows are stored in MFMA lane order:
+// physical row p holds key (p & ~31) | key_perm(p & 31).  A stage is a whole
+// number of 1 KB blocks, the unit of a wave's direct global->LDS load.
 template <int D>
 struct Lds {
-  static constexpr int KE = kKC * D;       // K elements per stage
-  static constexpr int VE = D * kKC;       // V^T elements per stage
+  static constexpr int KROW = D + 8;          // elements per K row (padded)
+  static constexpr int VROW = kKC + 8;        // elements per V^T row (padded)
+  static constexpr int KE = kKC * KROW;       // K elements per stage
+  static constexpr int VE = D * VROW;         // V^T elements per stage
   static constexpr int STAGE = KE + VE;
-  static constexpr int KC16 = D / 8;       // 16-byte columns per K row
-  static constexpr int VC16 = kKC / 8;     // 16-byte columns per V^T row (8)
-  // K row r (key), 16-byte column c -> element offset
+  static constexpr int KC16 = D / 8;          // 16-byte data units per K row
+  static constexpr int VC16 = kKC / 8;        // 16-byte data units per V^T row
+  static_assert(KE % 512 == 0 && VE % 512 == 0, "stage parts are whole 1 KB blocks");
+  // key r of the chunk, 16-byte column c -> element offset
   __device__ __forceinline__ static int k_off(int r, int c) {
-    return r * D + ((c ^ (key_perm(r & 31) & (KC16 - 1))) << 3);
+    return ((r & ~31) | key_perm(r & 31)) * KROW + c * 8;
   }
-  // V^T row d (channel), 16-byte column c (8 keys) -> element offset
-  __device__ __forceinline__ static int v_off(int d, int c) {
-    return d * kKC + ((c ^ ((d & 7) ^ ((d >> 3) & 1))) << 3);
-  }
+  // V^T row d (channel), 16-byte column c (keys 8c .. 8c+7) -> element offset
+  __device__ __forceinline__ static int v_off(int d, int c) { return d * VROW + c * 8; }
 };
 
-// QT 32-query column tiles per wave: every K / V^T fragment read from LDS
-// feeds QT MFMAs, which divides the LDS read traffic per FLOP by QT.
-template <int D, int QT = 1>
+// A wave's flash-attention state for 32 query rows.
+//
+// Online softmax with a lazily raised, integer offset: probabilities are
+// p = 2^(c2 s - mo) with c2 = scale * log2(e) and mo an integer held per
+// query.  mo is raised (to the ceiling of the running max of c2 s) only when
+// some score exceeds it by more than 8, so every p stays <= 256, and every
+// rescale factor 2^(mo_old - mo_new) is a power of two: rescaling the
+// accumulators, the row sum and already rounded bf16 probabilities is exact.
+// The final normalisation divides by the sum of the rounded probabilities
+// that were actually multiplied with V.
+template <int D>
 struct WaveState {
   static constexpr int DK = D / 16;  // MFMA k-steps over the head dimension
   static constexpr int DT = D / 32;  // 32-row blocks of O^T
-  bf16x8 qf[QT][DK];                 // Q fragments (B operand: k = head dim, n = query)
-  f32x16 acc[QT][DT];                // O^T accumulators
-  float m_run[QT];                   // running max (raw score units)
-  float l_part[QT];                  // this lane half's partial row sum
+  bf16x8 qf[DK];                     // Q fragments (B operand: k = head dim, n = query)
+  f32x16 acc[DT];                    // O^T accumulators
+  float mo;                          // offset in exp2 units (integer valued; -inf before any key)
+  float l_part;                      // this lane half's partial row sum
 
-  // q_ptr(qt) points at the query row of column tile qt owned by this lane.
-  template <class QPtr>
-  __device__ __forceinline__ void init(QPtr q_ptr, int hi) {
+  // qrow_ptr points at the query row owned by this lane.
+  __device__ __forceinline__ void init(const uint16_t* qrow_ptr, int hi) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const uint16_t* p = q_ptr(qt);
+    for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow_ptr + kk * 16 + hi * 8);
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qf[qt][kk] = *reinterpret_cast<const bf16x8*>(p + kk * 16 + hi * 8);
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    mo = -INFINITY;
+    l_part = 0.f;
+  }
+
+  // S^T = K Q^T for the 32 keys kb*32 .. kb*32+31 of the staged chunk
+  // (lane col reads physical row kb*32 + col): all K fragments, then the
+  // MFMA chain.
+  __device__ __forceinline__ f32x16 scores(const uint16_t* lk, int kb, int col, int hi) const {
+    const uint16_t* kp = lk + (kb * 32 + col) * Lds<D>::KROW + hi * 8;
+    bf16x8 ka[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < DK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+    // at most four fragment reads ahead of the MFMA chain (register budget)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int kk = 0; kk < DK - 4; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    return s;
+  }
+
+  // Keys at or past nk (< 32) of a block get -inf.  Register r holds key
+  // 16*(r/8) + 8*hi + r%8, invalid when 16*(r/8) + r%8 >= nk - 8*hi; the
+  // threshold is laundered through an empty asm so that the compares stay
+  // against immediates (no per-register key constants kept live).
+  __device__ __forceinline__ static void mask(f32x16& s, int nk, int hi) {
+    int thr = nk - 8 * hi;
+    asm volatile("" : "+v"(thr));
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (16 * (r >> 3) + (r & 7) >= thr) s[r] = -INFINITY;
+  }
+
+  // Raise the offset if some score of s exceeds it by more than 8 (a wave
+  // vote; both lane halves of a query take the same new offset).  The
+  // accumulators, the row sum and the probabilities of a block whose V
+  // product is still pending (pend, may be null) are rescaled.
+  __device__ __forceinline__ void raise(const f32x16& s, float c2, bf16x8* pend) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float mxc = mx * c2;
+    if (__any(mxc - mo > 8.0f)) {
+      const float mn = fmaxf(mo, ceilf(fmaxf(mxc, __shfl_xor(mxc, 32))));
+      // 2^(mo - mn) exactly; 0 before the first key (nothing accumulated yet)
+      const float alpha = mo == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.0f, (int)(mo - mn));
+      l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[qt][dt][r] = 0.f;
-      m_run[qt] = -INFINITY;
-      l_part[qt] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      if (pend) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pend[h][t] = (__bf16)((float)pend[h][t] * alpha);
+      }
+      mo = mn;
     }
-  }
-  __device__ __forceinline__ void init(const uint16_t* qrow_ptr, int hi) {
-    init([&](int qt) { return qrow_ptr + (long)qt * 32 * D; }, hi);
   }
 
-  // One 32-key block (keys kb*32 .. kb*32+31 of the staged chunk), of which
-  // the first nk are valid.  c2 = softmax scale * log2(e).
-  __device__ __forceinline__ void block32(const uint16_t* lk, const uint16_t* lvt, int kb, int nk,
-                                          float c2, int col, int hi) {
-    // S^T = K Q^T for 32 keys x 32 queries, one query column tile at a time
-    // (K fragments read from LDS once and reused by every tile), followed
-    // directly by that tile's softmax so only one S tile is live.
-    const int row = kb * 32 + key_perm(col);
-    bf16x8 ka[DK];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-      ka[kk] = *reinterpret_cast<const bf16x8*>(lk + Lds<D>::k_off(row, 2 * kk + hi));
-    bf16x8 pb[QT][2];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[qt][0], f32x16{}, 0, 0, 0);
-#pragma unroll
-      for (int kk = 1; kk < DK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[qt][kk], s, 0, 0, 0);
-      // keys past the valid count (only in a tile's last block)
-      if (nk < 32) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (16 * (r >> 3) + 8 * hi + (r & 7) >= nk) s[r] = -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      // Lazy rescaling: the running max (the same value in both lane halves
-      // of a query) is raised only when some score exceeds it by more than
-      // 2^8 in exp2 units, so every probability stays <= 256 and the final
-      // normalisation by the same running sum is exact.  The decision needs
-      // only each lane's own 16 keys and a wave vote; the exchange between
-      // the two halves happens only on the (rare) raise.
-      if (__any((mx - m_run[qt]) * c2 > 8.0f)) {
-        const float m_new = fmaxf(m_run[qt], fmaxf(mx, __shfl_xor(mx, 32)));
-        const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - m_new) * c2);
-        l_part[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[qt][dt][r] *= alpha;
-        m_run[qt] = m_new;
-      }
-      const float mc = m_run[qt] * c2;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          pb[qt][half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mc));
-        // row sum of the rounded probabilities actually multiplied with V
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          bf16x2 pr = {pb[qt][half][t], pb[qt][half][t + 1]};
-          l_part[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part[qt], false);
-        }
-      }
-      // keep the scheduler from overlapping several tiles' S (register bound)
-      if (QT > 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // O^T += V^T P^T
+  // Probabilities of a block as the bf16 B operands of the two 16-key steps,
+  // and their (rounded) sum added to the row sum.
+  __device__ __forceinline__ void probs(const f32x16& s, float c2, bf16x8 pb[2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int ks = kb * 2 + half;  // 16-key step inside the chunk
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(lvt + Lds<D>::v_off(dt * 32 + col, 2 * ks + hi));
+      for (int t = 0; t < 8; ++t) pb[half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mo));
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt][half], acc[qt][dt], 0, 0, 0);
+      for (int t = 0; t < 8; t += 2) {
+        bf16x2 pr = {pb[half][t], pb[half][t + 1]};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
       }
     }
   }
 
-  // One staged chunk with ck valid keys (1..64).
-  __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
-                                        int col, int hi) {
-    block32(lk, lvt, 0, min(ck, 32), c2, col, hi);
-    if (ck > 32) block32(lk, lvt, 1, ck - 32, c2, col, hi);
+  // O^T += V^T P^T for block kb.  Lane col reads channel row dt*32 + col,
+  // keys 16*ks + 8*hi .. +7 of the 16-key step ks = 2*kb + half.
+  __device__ __forceinline__ void pv(const uint16_t* lvt, int kb, int col, int hi, const bf16x8 pb[2]) {
+    const uint16_t* vp = lvt + col * Lds<D>::VROW + kb * 32 + hi * 8;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], acc[dt], 0, 0, 0);
+      }
   }
 
-  // Normalise and write the query row of column tile qt (d channels, bf16)
-  // to op.  Both lane halves must call it (they exchange partial sums).
-  __device__ __forceinline__ void store(int qt, uint16_t* op, int hi, bool write) {
-    const float l_tot = l_part[qt] + __shfl_xor(l_part[qt], 32);
+  // One staged chunk with ck valid keys (1..64).  A full chunk is software
+  // pipelined over its two 32-key blocks: the first block's V product is
+  // independent of the second block's softmax, so the two can overlap.
+  __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
+                                        int col, int hi) {
+    f32x16 s0 = scores(lk, 0, col, hi);
+    if (ck < 32) mask(s0, ck, hi);
+    raise(s0, c2, nullptr);
+    bf16x8 p0[2];
+    probs(s0, c2, p0);
+    pv(lvt, 0, col, hi, p0);
+    if (ck > 32) {
+      f32x16 s1 = scores(lk, 1, col, hi);
+      if (ck < 64) mask(s1, ck - 32, hi);
+      raise(s1, c2, nullptr);
+      bf16x8 p1[2];
+      probs(s1, c2, p1);
+      pv(lvt, 1, col, hi, p1);
+    }
+  }
+
+  // Normalise and write this lane's query row (d channels, bf16) to op.
+  // Both lane halves must call it (they exchange partial sums).
+  __device__ __forceinline__ void store(uint16_t* op, int hi, bool write) {
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
     if (!write) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -184,7 +216,7 @@ struct WaveState {
         const int d0 = dt * 32 + 8 * r4 + 4 * hi;
         __bf16 h[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[qt][dt][4 * r4 + x] * inv);
+        for (int x = 0; x < 4; ++x) h[x] = (__bf16)(acc[dt][4 * r4 + x] * inv);
         uint2 pk;
         pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
@@ -194,7 +226,6 @@ struct WaveState {
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t* op, int hi, bool write) { store(0, op, hi, write); }
 };
 
 }  // namespace core
