@@ -125,15 +125,16 @@ struct ChunkLoader {
   static constexpr int PER = (NI + NW - 1) / NW;
   static_assert(KU % 64 == 0 && VU % 64 == 0, "whole instructions per part");
   int wave;           // wave-uniform
+  int lane;
   int off_full[PER];  // source element offsets of this lane's pieces, 64-key chunk
-  int off_half[PER];  // the same for a 32-key chunk
 
   __device__ __forceinline__ static int ins_of(int wave, int x) {
     return min(wave + x * NW, NI - 1);  // past the last: clamped, never issued
   }
 
-  __device__ __forceinline__ void init(int w, int lane, int slots) {
+  __device__ __forceinline__ void init(int w, int ln, int slots) {
     wave = __builtin_amdgcn_readfirstlane(w);
+    lane = ln;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int ins = ins_of(wave, x);
@@ -143,15 +144,23 @@ struct ChunkLoader {
         const int c = min(u % (Lds<D>::KC16 + 1), Lds<D>::KC16 - 1);
         const int key = (p & ~31) | core::key_perm(p & 31);
         off_full[x] = key * D + c * 8;
-        off_half[x] = min(key, 31) * D + c * 8;
       } else {
         const int v = u - KU;
         const int d = v / (Lds<D>::VC16 + 1);
         const int c = min(v % (Lds<D>::VC16 + 1), Lds<D>::VC16 - 1);
         off_full[x] = d * slots + c * 8;
-        off_half[x] = d * slots + min(c, 3) * 8;
       }
     }
+  }
+
+  // The source offset of piece x for a 32-key chunk: K rows past 31 and V^T
+  // key columns past 31 are clamped to the last valid ones (derived from the
+  // 64-key offset: K rows are D apart, the V^T column unit is recomputed).
+  __device__ __forceinline__ int off_half(int x) const {
+    const int ins = ins_of(wave, x);
+    if (ins < KI) return min(off_full[x], 31 * D + (off_full[x] & (D - 1)));
+    const int c = min((ins * 64 + lane - KU) % (Lds<D>::VC16 + 1), Lds<D>::VC16 - 1);
+    return off_full[x] - max(c - 3, 0) * 8;
   }
 
   __device__ __forceinline__ void issue(uint16_t* stage, const uint16_t* __restrict__ kbase,
@@ -161,7 +170,7 @@ struct ChunkLoader {
       if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
       const uint16_t* base = ins < KI ? kbase : vbase;
-      __builtin_amdgcn_global_load_lds(base + (half ? off_half[x] : off_full[x]),
+      __builtin_amdgcn_global_load_lds(base + (half ? off_half(x) : off_full[x]),
                                        (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
     }
   }

@@ -182,9 +182,7 @@ struct WaveState {
       }
   }
 
-  // One staged chunk with ck valid keys (1..64).  A full chunk is software
-  // pipelined over its two 32-key blocks: the first block's V product is
-  // independent of the second block's softmax, so the two can overlap.
+  // One staged chunk with ck valid keys (1..64), block by block.
   __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
                                         int col, int hi) {
     f32x16 s0 = scores(lk, 0, col, hi);
