@@ -115,50 +115,74 @@ __global__ __launch_bounds__(D) void fine_qbar_kernel(Geo g, const uint16_t* __r
 }
 
 constexpr int kScoreGroups = 16;
+constexpr int kScoreKeys = 4;
 
-// Scores of 16 groups x 256 keys per workgroup; one key per thread, the 16
-// group means are wave-uniform (scalar loads).
+// Scores of 16 groups x 1024 keys per workgroup, four keys per thread (keys
+// 256 apart, so every load instruction is coalesced).  The 16 group means
+// are staged channel-major in LDS and read as wave-wide broadcasts, each
+// feeding 4 keys x 2 groups of fp64 FMAs.  Every score is the sequential
+// fp64 sum over channels c = 0 .. D-1 of the exact products qbar[c] * k[c].
 template <int D>
-__global__ __launch_bounds__(256) void fine_score_kernel(Geo g, const uint16_t* __restrict__ k,
-                                                         const double* __restrict__ qbar64,
-                                                         double* __restrict__ score, FineScratch f) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256, 2) void fine_score_kernel(Geo g, const uint16_t* __restrict__ k,
+                                                            const double* __restrict__ qbar64,
+                                                            double* __restrict__ score, FineScratch f) {
+  __shared__ __align__(16) double qs[D][kScoreGroups];
   const int g0 = blockIdx.y * kScoreGroups;
   const long bh = blockIdx.z;
   const int ng = min(kScoreGroups, g.fine_G - g0);
-  const bool valid = j < g.N;
-  const uint16_t* kr = k + (bh * (long)g.N + (valid ? j : 0)) * D;
-  double acc[kScoreGroups];
-#pragma unroll
-  for (int x = 0; x < kScoreGroups; ++x) acc[x] = 0.0;
   const double* qb = qbar64 + (bh * g.fine_G + g0) * (long)D;
-  // channels in order c = 0..D-1 for every group; 8 channels per 16-byte load
+  for (int i = threadIdx.x; i < D * kScoreGroups; i += 256) {
+    const int x = i / D, c = i % D;
+    qs[c][x] = x < ng ? qb[(long)x * D + c] : 0.0;
+  }
+  __syncthreads();
+  const int jb = blockIdx.x * 256 * kScoreKeys + threadIdx.x;
+  const uint16_t* kr[kScoreKeys];
+#pragma unroll
+  for (int t = 0; t < kScoreKeys; ++t) kr[t] = k + (bh * (long)g.N + min(jb + 256 * t, g.N - 1)) * D;
+  double acc[kScoreKeys][kScoreGroups];
+#pragma unroll
+  for (int t = 0; t < kScoreKeys; ++t)
+#pragma unroll
+    for (int x = 0; x < kScoreGroups; ++x) acc[t][x] = 0.0;
   for (int p8 = 0; p8 < D / 8; ++p8) {
-    const u32x4 w4 = *reinterpret_cast<const u32x4*>(kr + p8 * 8);
+    u32x4 w4[kScoreKeys];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = w4[e];
-      const double k0 = (double)__uint_as_float(w << 16);
-      const double k1 = (double)__uint_as_float(w & 0xffff0000u);
-      const int c = p8 * 8 + 2 * e;
+    for (int t = 0; t < kScoreKeys; ++t) w4[t] = *reinterpret_cast<const u32x4*>(kr[t] + p8 * 8);
 #pragma unroll
-      for (int x = 0; x < kScoreGroups; ++x)
-        if (x < ng) acc[x] = fma(qb[(long)x * D + c], k0, acc[x]);
+    for (int e = 0; e < 8; ++e) {
+      const int c = p8 * 8 + e;
+      double kv[kScoreKeys];
 #pragma unroll
-      for (int x = 0; x < kScoreGroups; ++x)
-        if (x < ng) acc[x] = fma(qb[(long)x * D + c + 1], k1, acc[x]);
+      for (int t = 0; t < kScoreKeys; ++t) {
+        const uint32_t w = w4[t][e >> 1];
+        kv[t] = (double)__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+      }
+#pragma unroll
+      for (int x = 0; x < kScoreGroups; x += 2) {
+        const double2 qq = *reinterpret_cast<const double2*>(&qs[c][x]);
+#pragma unroll
+        for (int t = 0; t < kScoreKeys; ++t) {
+          acc[t][x] = fma(qq.x, kv[t], acc[t][x]);
+          acc[t][x + 1] = fma(qq.y, kv[t], acc[t][x + 1]);
+        }
+      }
     }
   }
   unsigned long long kmin = ~0ull, kmax = 0ull;
-  if (valid) {
-    double* dst = score + (bh * g.fine_G + g0) * (long)g.N + j;
 #pragma unroll
-    for (int x = 0; x < kScoreGroups; ++x) {
-      if (x < ng) {
-        dst[(long)x * g.N] = acc[x];
-        const unsigned long long kk = okey(acc[x]);
-        kmin = min(kmin, kk);
-        kmax = max(kmax, kk);
+  for (int t = 0; t < kScoreKeys; ++t) {
+    const int j = jb + 256 * t;
+    if (j < g.N) {
+      double* dst = score + (bh * g.fine_G + g0) * (long)g.N + j;
+#pragma unroll
+      for (int x = 0; x < kScoreGroups; ++x) {
+        if (x < ng) {
+          dst[(long)x * g.N] = acc[t][x];
+          const unsigned long long kk = okey(acc[t][x]);
+          kmin = min(kmin, kk);
+          kmax = max(kmax, kk);
+        }
       }
     }
   }
@@ -476,7 +500,7 @@ hipError_t launch_fine_select(const Geo& g, const Ws& w, const uint16_t* q, cons
   else
     hipLaunchKernelGGL(fine_qbar_kernel<64>, dim3(g.fine_G, BH), dim3(64), 0, s, g, q, w.fine_qbar, f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 sg((g.N + 255) / 256, (g.fine_G + kScoreGroups - 1) / kScoreGroups, BH);
+  dim3 sg((g.N + 256 * kScoreKeys - 1) / (256 * kScoreKeys), (g.fine_G + kScoreGroups - 1) / kScoreGroups, BH);
   double* score = reinterpret_cast<double*>(w.fine_score);
   if (g.d == 128)
     hipLaunchKernelGGL(fine_score_kernel<128>, sg, dim3(256), 0, s, g, k, f.qbar64, score, f);
