@@ -126,14 +126,29 @@ struct WaveState {
       if (16 * (r >> 3) + (r & 7) >= thr) s[r] = -INFINITY;
   }
 
-  // Raise the offset if some score of s exceeds it by more than 8 (a wave
-  // vote; both lane halves of a query take the same new offset).  The
-  // accumulators, the row sum and the probabilities of a block whose V
-  // product is still pending (pend, may be null) are rescaled.
-  __device__ __forceinline__ void raise(const f32x16& s, float c2, bf16x8* pend) {
-    float mx = s[0];
+  // Probabilities of a block against the current offset, as the bf16 B
+  // operands of the two 16-key steps.
+  __device__ __forceinline__ void probs(const f32x16& s, float c2, bf16x8 pb[2]) const {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pb[half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mo));
+  }
+
+  // Softmax of one block.  The probabilities are computed against the
+  // current offset while this lane's block max is reduced (a three-level
+  // tree); the offset is raised, and the probabilities recomputed, only
+  // when some score exceeds it by more than 8 in exp2 units (a wave vote;
+  // both lane halves of a query take the same new offset), so every
+  // probability stays <= 256.  The rounded probabilities are then summed
+  // into the row sum.
+  __device__ __forceinline__ void softmax(const f32x16& s, float c2, bf16x8 pb[2]) {
+    probs(s, c2, pb);
+    float m3[6];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(s[3 * k], s[3 * k + 1]), s[3 * k + 2]);
+    m3[5] = s[15];
+    const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
     const float mxc = mx * c2;
     if (__any(mxc - mo > 8.0f)) {
       const float mn = fmaxf(mo, ceilf(fmaxf(mxc, __shfl_xor(mxc, 32))));
@@ -144,29 +159,17 @@ struct WaveState {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      if (pend) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pend[h][t] = (__bf16)((float)pend[h][t] * alpha);
-      }
       mo = mn;
+      probs(s, c2, pb);
     }
-  }
-
-  // Probabilities of a block as the bf16 B operands of the two 16-key steps,
-  // and their (rounded) sum added to the row sum.
-  __device__ __forceinline__ void probs(const f32x16& s, float c2, bf16x8 pb[2]) {
+    // row sum of the rounded probabilities actually multiplied with V
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pb[half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -mo));
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
         bf16x2 pr = {pb[half][t], pb[half][t + 1]};
         l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l_part, false);
       }
-    }
   }
 
   // O^T += V^T P^T for block kb.  Lane col reads channel row dt*32 + col,
@@ -187,16 +190,14 @@ struct WaveState {
                                         int col, int hi) {
     f32x16 s0 = scores(lk, 0, col, hi);
     if (ck < 32) mask(s0, ck, hi);
-    raise(s0, c2, nullptr);
     bf16x8 p0[2];
-    probs(s0, c2, p0);
+    softmax(s0, c2, p0);
     pv(lvt, 0, col, hi, p0);
     if (ck > 32) {
       f32x16 s1 = scores(lk, 1, col, hi);
       if (ck < 64) mask(s1, ck - 32, hi);
-      raise(s1, c2, nullptr);
       bf16x8 p1[2];
-      probs(s1, c2, p1);
+      softmax(s1, c2, p1);
       pv(lvt, 1, col, hi, p1);
     }
   }
