@@ -360,13 +360,15 @@ template <int D, int NW>
 struct GatherLoader {
   static constexpr int P = D / 8;                  // 16-byte pieces per row
   static constexpr int T = NW * 64;
-  static constexpr int NP = (kKC * P + T - 1) / T; // pieces per thread per tensor
+  static constexpr int NP = (kKC * P + T - 1) / T; // K pieces per thread
+  static constexpr int NQ = (kKC / 4 * P + T - 1) / T;  // V quads (4 keys x 8 channels) per thread
   u32x4 kr[NP];
-  u32x4 vr[NP];
+  u32x4 vr[NQ][4];
 
-  // K pieces: piece-fastest (a key row is read by consecutive lanes);
-  // V pieces: key-fastest (consecutive lanes write consecutive keys of one
-  // transposed LDS row).  Rows past the chunk re-read its last valid key.
+  // K pieces: piece-fastest (a key row is read by consecutive lanes).
+  // V quads: 4 consecutive keys x 8 channels per thread, key quads fastest,
+  // so that 16 lanes write one 128-byte run of a transposed LDS row.  Rows
+  // past the chunk re-read its last valid key.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
                                        const int* __restrict__ keys, int nk) {
     const int tid = threadIdx.x;
@@ -375,8 +377,14 @@ struct GatherLoader {
       const int pc = min(tid + x * T, kKC * P - 1);
       const int kr_row = min(pc / P, nk - 1), kp = pc % P;
       kr[x] = *reinterpret_cast<const u32x4*>(kh + (long)keys[kr_row] * D + kp * 8);
-      const int vr_row = min(pc % kKC, nk - 1), vp = pc / kKC;
-      vr[x] = *reinterpret_cast<const u32x4*>(vh + (long)keys[vr_row] * D + vp * 8);
+    }
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int qd = min(tid + x * T, kKC / 4 * P - 1);
+      const int j = qd % (kKC / 4), p = qd / (kKC / 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vr[x][t] = *reinterpret_cast<const u32x4*>(vh + (long)keys[min(4 * j + t, nk - 1)] * D + p * 8);
     }
   }
 
@@ -388,13 +396,23 @@ struct GatherLoader {
     for (int x = 0; x < NP; ++x) {
       const int pc = min(tid + x * T, kKC * P - 1);
       *reinterpret_cast<u32x4*>(lk + Lds<D>::k_off(pc / P, pc % P)) = kr[x];
-      const int r = pc % kKC, p = pc / kKC;
+    }
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int qd = min(tid + x * T, kKC / 4 * P - 1);
+      const int j = qd % (kKC / 4), p = qd / (kKC / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vr[x][e];
+        // channels p*8 + 2e (low halves) and p*8 + 2e + 1 (high halves) of keys 4j .. 4j+3
+        const uint32_t w0 = vr[x][0][e], w1 = vr[x][1][e], w2 = vr[x][2][e], w3 = vr[x][3][e];
+        uint2 lo, hi;
+        lo.x = (w0 & 0xffffu) | (w1 << 16);
+        lo.y = (w2 & 0xffffu) | (w3 << 16);
+        hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
+        hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
         const int d0 = p * 8 + 2 * e;
-        lvt[Lds<D>::v_off(d0, r >> 3) + (r & 7)] = (uint16_t)(w & 0xffffu);
-        lvt[Lds<D>::v_off(d0 + 1, r >> 3) + (r & 7)] = (uint16_t)(w >> 16);
+        *reinterpret_cast<uint2*>(lvt + Lds<D>::v_off(d0, 0) + 4 * j) = lo;
+        *reinterpret_cast<uint2*>(lvt + Lds<D>::v_off(d0 + 1, 0) + 4 * j) = hi;
       }
     }
   }
@@ -424,8 +442,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
   const int n = ptr[bh * (g.fine_G + 1) + gi + 1] - lo;
   const int* keys = idx + bh * g.fine_cap + lo;
 
+  // One LDS stage: the next chunk's rows are gathered into registers while
+  // the current one is multiplied, then written over it between two
+  // barriers (a small stage lets four workgroups share a CU).
   GatherLoader<D, NW> ld;
-  int stage = 0;
   if (n > 0) {
     ld.load(k + head, v + head, keys, min(kKC, n));
     ld.store(lds);
@@ -435,11 +455,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
     const int e1 = e0 + kKC;
     const bool has_next = e1 < n;
     if (has_next) ld.load(k + head, v + head, keys + e1, min(kKC, n - e1));
-    const uint16_t* lk = lds + stage * Lds<D>::STAGE;
-    if (active) ws.chunk(lk, lk + Lds<D>::KE, min(kKC, n - e0), c2, col, hi);
-    if (has_next) ld.store(lds + (stage ^ 1) * Lds<D>::STAGE);
-    __syncthreads();
-    stage ^= 1;
+    if (active) ws.chunk(lds, lds + Lds<D>::KE, min(kKC, n - e0), c2, col, hi);
+    if (has_next) {
+      __syncthreads();
+      ld.store(lds);
+      __syncthreads();
+    }
   }
   if (!active) return;
   const bool valid = row0 + col < rows_end;
@@ -449,7 +470,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
 template <int D, int NW>
 hipError_t launch_fine_attend_t(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, uint16_t* o, hipStream_t s) {
-  const size_t shmem = 2 * Lds<D>::STAGE * sizeof(uint16_t);
+  const size_t shmem = Lds<D>::STAGE * sizeof(uint16_t);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fine_attend_kernel<D, NW>),
