@@ -171,6 +171,8 @@ def main():
     ms_layout = stage(lambda: plan.layout(q, k, v), n_st)
     ms_select = stage(lambda: plan.select(q, k, v), n_st)
     ms_attend = stage(lambda: plan.attend(o, q, k, v), n_st)
+    # a whole call that reuses the mask already in the workspace
+    ms_cached = stage(lambda: plan.forward_cached(q, k, v, o), n_st)
 
     BH = wl.B * wl.H
     # read Q, K, V + write the tile-major copies (no layout stage for the
@@ -208,6 +210,7 @@ def main():
                    "retained_flops": flops, "parallelism": "single GPU"},
         "stages_ms": {"layout": round(ms_layout, 4), "select": round(ms_select, 4),
                       "attend": round(ms_attend, 4)},
+        "ms_per_call_cached_mask": round(ms_cached, 4),
         "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1) if bytes_layout else None,
         "layout_hbm_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                             if bytes_layout else None),

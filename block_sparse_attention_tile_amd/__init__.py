@@ -10,7 +10,7 @@ from . import _lib
 from ._lib import (  # noqa: F401
     VSA_DENSE, VSA_FINE, VSA_SICS_SELECT, VSA_TOPK, VSA_TOPK_FRAC, VSA_TOPP, VSA_WINDOW,
     VSA_WIN_CLAMP, VSA_WIN_TRUNCATE, VsaError, lib, make_policy, make_problem, vsa_attend,
-    vsa_forward, vsa_layout, vsa_plan, vsa_plan_destroy, vsa_plan_get_info,
+    vsa_forward, vsa_forward_cached, vsa_layout, vsa_plan, vsa_plan_destroy, vsa_plan_get_info,
     vsa_read_selection, vsa_retained_work, vsa_select, vsa_untile, vsa_workspace_bytes,
     vsa_workspace_region,
 )
@@ -76,6 +76,17 @@ class Plan:
         self._check(q, k, v, o)
         vsa_forward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(self.workspace()),
                     self.ws_bytes, self._stream())
+        return o
+
+    def forward_cached(self, q, k, v, o=None):
+        """Forward against the selection already in this plan's workspace
+        (from the last forward/select): see vsa_forward_cached."""
+        import torch
+        if o is None:
+            o = torch.empty_like(q)
+        self._check(q, k, v, o)
+        vsa_forward_cached(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(self.workspace()),
+                           self.ws_bytes, self._stream())
         return o
 
     def layout(self, q, k, v):

@@ -37,7 +37,7 @@ VSA_MAX_CAND = 4
 
 EXPORTED = [
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_workspace_bytes",
-    "vsa_workspace_region", "vsa_forward", "vsa_layout", "vsa_select", "vsa_attend",
+    "vsa_workspace_region", "vsa_forward", "vsa_forward_cached", "vsa_layout", "vsa_select", "vsa_attend",
     "vsa_untile", "vsa_read_selection", "vsa_retained_work", "vsa_status_string",
     "vsa_last_error",
 ]
@@ -93,7 +93,7 @@ def lib():
     L.vsa_workspace_region.argtypes = [P, C.c_int, C.POINTER(sz), C.POINTER(sz)]
     for name in ("vsa_layout", "vsa_select"):
         getattr(L, name).argtypes = [P, P, P, P, P, sz, P]
-    for name in ("vsa_forward", "vsa_attend"):
+    for name in ("vsa_forward", "vsa_forward_cached", "vsa_attend"):
         getattr(L, name).argtypes = [P, P, P, P, P, P, sz, P]
     L.vsa_untile.argtypes = [P, C.c_int, P, sz, P, P]
     L.vsa_read_selection.argtypes = [P, P, sz, C.POINTER(C.c_int32), C.POINTER(C.c_int32), sz,
@@ -183,6 +183,10 @@ def vsa_workspace_region(plan, region):
 
 def vsa_forward(plan, q, k, v, o, ws, ws_bytes, stream):
     _check(lib().vsa_forward(plan, q, k, v, o, ws, ws_bytes, stream))
+
+
+def vsa_forward_cached(plan, q, k, v, o, ws, ws_bytes, stream):
+    _check(lib().vsa_forward_cached(plan, q, k, v, o, ws, ws_bytes, stream))
 
 
 def vsa_layout(plan, q, k, v, ws, ws_bytes, stream):

@@ -324,17 +324,20 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   return VSA_OK;
 }
 
+// Tile layout of q, k, v.  With mask inputs (the default) it also runs the
+// SICS blocking choice and the pooled means the selection needs; a cached
+// call (mask = false) keeps the blocking and the selection in the workspace.
 int enqueue_layout(const vsa_plan_t* p, const void* q, const void* k, const void* v, void* ws,
-                   hipStream_t s) {
+                   hipStream_t s, bool mask = true) {
   const Geo& g = p->geo;
   if (g.flags & VSA_FINE) return VSA_OK;
   Ws w = resolve(p, ws);
   hipError_t e;
-  if (g.flags & VSA_SICS_SELECT) {
+  if (mask && (g.flags & VSA_SICS_SELECT)) {
     e = vsa::launch_sics(g, w, (const uint16_t*)q, (const uint16_t*)k, s);
     if (e != hipSuccess) return hip_fail(e, "SICS kernels");
   }
-  bool pool = (g.flags & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) != 0;
+  bool pool = mask && (g.flags & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) != 0;
   e = vsa::launch_layout(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pool, s);
   if (e != hipSuccess) return hip_fail(e, "layout kernel");
   return VSA_OK;
@@ -480,6 +483,20 @@ int vsa_forward(const vsa_plan_t* p, const void* q, const void* k, const void* v
   hipStream_t s = (hipStream_t)stream;
   if ((st = enqueue_layout(p, q, k, v, ws, s))) return st;
   if ((st = enqueue_select(p, q, k, ws, s))) return st;
+  if ((st = enqueue_attend(p, q, k, v, o, ws, s))) return st;
+  return ok();
+}
+
+int vsa_forward_cached(const vsa_plan_t* p, const void* q, const void* k, const void* v, void* o,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int st = check_exec(p, ws, ws_bytes);
+  if (st) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(o, "o")))
+    return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = enqueue_layout(p, q, k, v, ws, s, /*mask=*/false))) return st;
   if ((st = enqueue_attend(p, q, k, v, o, ws, s))) return st;
   return ok();
 }

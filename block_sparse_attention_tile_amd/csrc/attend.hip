@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   const int sb = item % nsb;
   const int i = (item / nsb) % g.max_tiles;
   const long bh = item / (nsb * g.max_tiles);
-  if (cand && cand[bh] != blocking) return;
+  if (cand_of(g, cand, bh) != blocking) return;
   const BlkGeo b = pick_blk(g, blocking);
   if (i >= b.n_tiles) return;
   const int slots = b.slots;
@@ -221,10 +221,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 
   // kept-tile list -> LDS (after the K/V stages)
   int* cols = reinterpret_cast<int*>(lds + STAGES * Lds<D>::STAGE);
-  const int L = row_len[bh * g.max_tiles + i];
+  // (row length and tile indices clamped: a selection that was never
+  // written still keeps every access in bounds)
+  const int L = min(max(row_len[bh * g.max_tiles + i], 0), g.row_cap);
   const int* gcols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
   for (int e = tid; e < L; e += NW * 64) {
-    const int j = gcols[e];
+    const int j = min(max(gcols[e], 0), b.n_tiles - 1);
     cols[e] = (tile_nvalid(g, b, j) << kTileBits) | j;
   }
 

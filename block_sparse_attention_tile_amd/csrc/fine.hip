@@ -369,6 +369,11 @@ struct GatherLoader {
   // V quads: 4 consecutive keys x 8 channels per thread, key quads fastest,
   // so that 16 lanes write one 128-byte run of a transposed LDS row.  Rows
   // past the chunk re-read its last valid key.
+  int n_tok;  // tokens per head (key indices are clamped below it)
+  __device__ __forceinline__ int key_at(const int* __restrict__ keys, int r) const {
+    return min(max(keys[r], 0), n_tok - 1);
+  }
+
   __device__ __forceinline__ void load(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
                                        const int* __restrict__ keys, int nk) {
     const int tid = threadIdx.x;
@@ -376,7 +381,7 @@ struct GatherLoader {
     for (int x = 0; x < NP; ++x) {
       const int pc = min(tid + x * T, kKC * P - 1);
       const int kr_row = min(pc / P, nk - 1), kp = pc % P;
-      kr[x] = *reinterpret_cast<const u32x4*>(kh + (long)keys[kr_row] * D + kp * 8);
+      kr[x] = *reinterpret_cast<const u32x4*>(kh + (long)key_at(keys, kr_row) * D + kp * 8);
     }
 #pragma unroll
     for (int x = 0; x < NQ; ++x) {
@@ -384,7 +389,7 @@ struct GatherLoader {
       const int j = qd % (kKC / 4), p = qd / (kKC / 4);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        vr[x][t] = *reinterpret_cast<const u32x4*>(vh + (long)keys[min(4 * j + t, nk - 1)] * D + p * 8);
+        vr[x][t] = *reinterpret_cast<const u32x4*>(vh + (long)key_at(keys, min(4 * j + t, nk - 1)) * D + p * 8);
     }
   }
 
@@ -438,14 +443,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
   core::WaveState<D> ws;
   if (active) ws.init(q + head + (long)qrow * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);
-  const int lo = ptr[bh * (g.fine_G + 1) + gi];
-  const int n = ptr[bh * (g.fine_G + 1) + gi + 1] - lo;
+  // (list bounds clamped to the capacity: a mask that was never written
+  // still keeps every access in bounds; key indices are clamped on load)
+  const int lo = min(max(ptr[bh * (g.fine_G + 1) + gi], 0), g.fine_cap);
+  const int n = min(max(ptr[bh * (g.fine_G + 1) + gi + 1] - lo, 0), g.fine_cap - lo);
   const int* keys = idx + bh * g.fine_cap + lo;
 
   // One LDS stage: the next chunk's rows are gathered into registers while
   // the current one is multiplied, then written over it between two
   // barriers (a small stage lets four workgroups share a CU).
   GatherLoader<D, NW> ld;
+  ld.n_tok = g.N;
   if (n > 0) {
     ld.load(k + head, v + head, keys, min(kKC, n));
     ld.store(lds);

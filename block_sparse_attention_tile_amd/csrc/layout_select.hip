@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
 
   const int i = blockIdx.x;
   const long bh = blockIdx.y;
-  const int c = cand ? cand[bh] : 0;
+  const int c = cand_of(g, cand, bh);
   const BlkGeo b = pick_blk(g, c);
   if (i >= b.n_tiles) return;
   const TileRef t = tile_ref(g, b, i);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kLayoutThreads) void untile_kernel(Geo g, const uin
   constexpr int P = D / 8;
   const int i = blockIdx.x;
   const long bh = blockIdx.y;
-  const int c = cand ? cand[bh] : 0;
+  const int c = cand_of(g, cand, bh);
   const BlkGeo b = pick_blk(g, c);
   if (i >= b.n_tiles) return;
   const TileRef t = tile_ref(g, b, i);
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
 
   const int i = blockIdx.x;
   const long bh = blockIdx.y;
-  const int c = cand ? cand[bh] : 0;
+  const int c = cand_of(g, cand, bh);
   const BlkGeo b = pick_blk(g, c);
   const int n = b.n_tiles;
   if (i >= n) return;

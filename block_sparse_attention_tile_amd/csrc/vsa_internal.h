@@ -47,6 +47,13 @@ struct Geo {
 __host__ __device__ __forceinline__ int sel4(int c, int a0, int a1, int a2, int a3) {
   return c == 0 ? a0 : (c == 1 ? a1 : (c == 2 ? a2 : a3));
 }
+// The blocking chosen for head bh (0 without SICS selection), clamped to a
+// valid index, so that a workspace whose selection was never written (a
+// cached call on a fresh workspace) still addresses memory in bounds.
+__device__ __forceinline__ int cand_of(const Geo& g, const int* cand, long bh) {
+  return cand ? min(max(cand[bh], 0), g.nb - 1) : 0;
+}
+
 __host__ __device__ __forceinline__ BlkGeo pick_blk(const Geo& g, int c) {
   BlkGeo b;
 #define VSA_PICK(f) b.f = sel4(c, g.blk[0].f, g.blk[1].f, g.blk[2].f, g.blk[3].f)

@@ -172,6 +172,19 @@ int vsa_workspace_region(const vsa_plan_t* plan, int region, size_t* offset, siz
 int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                 void* o, void* workspace, size_t ws_bytes, void* stream);
 
+/* Forward with a cached mask (the semi-static class of the SPADE review
+ * page, *What carries the argument*: a mask computed once and reused by later
+ * calls; the FG-Attn verdict page, pith_summary: a cached mask reused across
+ * denoising steps).  Lays out q, k, v and runs the attention against the
+ * selection already in `workspace`, written by the last vsa_forward or
+ * vsa_select on this workspace with this plan: no SICS choice (the blocking
+ * per head is kept), no pooled means, no selection.  Under VSA_FINE only the
+ * gathered attention runs.  Arguments, ownership and errors as vsa_forward.
+ * A workspace whose selection was never written gives unspecified output
+ * but no out-of-bounds access (lengths and indices are clamped in-kernel). */
+int vsa_forward_cached(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                       void* o, void* workspace, size_t ws_bytes, void* stream);
+
 /* Stage 1, layout: under VSA_SICS_SELECT scores every candidate blocking by
  * SICS and records the chosen one per head; then copies Q, K (tile-major)
  * and V (tile-major, transposed per tile) into the workspace, padding each
