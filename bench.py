@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--config", default="hunyuan")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--summarizer", choices=["mean", "max", "minmax"], default=None,
+                    help="override the workload's block summarizer (dynamic masks)")
+    ap.add_argument("--sink", type=int, default=None, help="override the workload's sink tiles")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -117,6 +120,10 @@ def main():
     from block_sparse_attention_tile_amd.workload import plan_structs as structs_of
 
     wl = CONFIGS[args.config]
+    if args.summarizer is not None:
+        wl = wl.with_(summarizer=args.summarizer)
+    if args.sink is not None:
+        wl = wl.with_(sink=args.sink)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
@@ -236,6 +243,10 @@ def _mask_desc(wl):
         parts.append("SICS blocking choice per head")
     if wl.fine_group:
         parts.append(f"fine M={wl.fine_group} keep {wl.fine_keep:.0%}")
+    if (wl.topk or wl.topk_frac or wl.topp) and wl.summarizer != "mean":
+        parts.append(f"{wl.summarizer} summarizer")
+    if wl.sink:
+        parts.append(f"sink {wl.sink} tiles")
     return ", ".join(parts) or "dense"
 
 

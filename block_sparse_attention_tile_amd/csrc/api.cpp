@@ -100,6 +100,7 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.vt = (uint16_t*)at(VSA_WS_VT);
   w.pooled_q = (float*)at(VSA_WS_POOLED_Q);
   w.pooled_k = (float*)at(VSA_WS_POOLED_K);
+  w.pooled_kmin = (float*)at(VSA_WS_POOLED_KMIN);
   w.row_len = (int*)at(VSA_WS_ROW_LEN);
   w.col_idx = (int*)at(VSA_WS_COL_IDX);
   w.cand = (int*)at(VSA_WS_CAND);
@@ -168,6 +169,14 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   g.scale = po->scale > 0 ? po->scale : 1.0 / std::sqrt((double)pr->d);
   g.win_mode = po->win_mode;
   g.topp = po->topp;
+  if (po->summarizer < VSA_SUMM_MEAN || po->summarizer > VSA_SUMM_MINMAX)
+    return fail(VSA_ERR_INVALID_ARG, "summarizer must be VSA_SUMM_MEAN, _MAX or _MINMAX (got %d)",
+                po->summarizer);
+  if (po->sink < 0) return fail(VSA_ERR_INVALID_ARG, "sink must be >= 0 (got %d)", po->sink);
+  if ((f & VSA_FINE) && po->sink > 0)
+    return fail(VSA_ERR_INVALID_ARG, "the tile sink does not apply to VSA_FINE");
+  g.summ = po->summarizer;
+  g.sink = po->sink;
 
   if (f & VSA_FINE) {
     int M = po->fine_group;
@@ -241,7 +250,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     if ((f & (VSA_DENSE | VSA_TOPP)) || (f & VSA_SICS_SELECT)) {
       g.row_cap = g.max_tiles;
     } else {
-      long cap = win_cells;
+      long cap = win_cells + g.sink;
       int maxk = 0;
       for (int c = 0; c < g.nb; ++c) maxk = std::max(maxk, g.blk[c].topk);
       cap += maxk;
@@ -273,6 +282,10 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
           for (int a = 0; a < 3; ++a)
             axis_range(c3[a], (g.win[a] - 1) / 2, b.nt[a], g.win_mode, &lo[a], &hi[a]);
         }
+        auto in_window = [&](int j) {
+          const int t = j / (b.nt[1] * b.nt[2]), h = (j / b.nt[2]) % b.nt[1], w = j % b.nt[2];
+          return t >= lo[0] && t <= hi[0] && h >= lo[1] && h <= hi[1] && w >= lo[2] && w <= hi[2];
+        };
         for (int t = lo[0]; t <= hi[0]; ++t)
           for (int h = lo[1]; h <= hi[1]; ++h)
             for (int w = lo[2]; w <= hi[2]; ++w) {
@@ -280,6 +293,11 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
               ++pairs;
               fl += (double)nv[i] * (double)nv[j];
             }
+        for (int j = 0; j < std::min(g.sink, b.n_tiles); ++j)  // sink tiles outside the window
+          if (!in_window(j)) {
+            ++pairs;
+            fl += (double)nv[i] * (double)nv[j];
+          }
       }
       p->static_pairs = pairs;
       p->static_flops = fl * 4.0 * g.d * g.B * g.H;
@@ -296,6 +314,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     sz[VSA_WS_QT] = sz[VSA_WS_KT] = sz[VSA_WS_VT] = tm;
     if (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) {
       sz[VSA_WS_POOLED_Q] = sz[VSA_WS_POOLED_K] = (size_t)BH * g.max_tiles * g.d * 4;
+      if (g.summ == VSA_SUMM_MINMAX) sz[VSA_WS_POOLED_KMIN] = sz[VSA_WS_POOLED_K];
     }
     sz[VSA_WS_ROW_LEN] = (size_t)BH * g.max_tiles * 4;
     sz[VSA_WS_COL_IDX] = (size_t)BH * g.max_tiles * g.row_cap * 4;

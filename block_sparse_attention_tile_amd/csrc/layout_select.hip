@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ qt, uint16_t* __restrict__ kt,
     uint16_t* __restrict__ vt, float* __restrict__ pooled_q, float* __restrict__ pooled_k,
-    const int* __restrict__ cand, int pool) {
+    float* __restrict__ pooled_kmin, const int* __restrict__ cand, int pool) {
   constexpr int P = D / 8;                       // 16-byte pieces per row
   constexpr int RPP = kLayoutThreads / P;        // rows per pass
   constexpr int LVW = D / 2 + 1;                 // V chunk row stride in words (odd: no bank conflicts)
@@ -88,8 +88,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
   const long tm_base = bh * g.tok_cap * D + (long)i * b.slots * D;
 
   double sq[8], sk[8];
+  float kmx[8], kmn[8];  // per-channel extrema of K over the valid tokens
 #pragma unroll
-  for (int x = 0; x < 8; ++x) sq[x] = sk[x] = 0.0;
+  for (int x = 0; x < 8; ++x) {
+    sq[x] = sk[x] = 0.0;
+    kmx[x] = -INFINITY;
+    kmn[x] = INFINITY;
+  }
+  const bool extrema = pool && g.summ != VSA_SUMM_MEAN;
 
   // Q and K: gather raster rows, store contiguous tile-major rows.
   for (int s0 = r0; s0 < b.slots; s0 += RPP * U) {
@@ -121,6 +127,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
           sq[2 * x + 1] += (double)bf16_hi(qw[x]);
           sk[2 * x] += (double)bf16_lo(kw[x]);
           sk[2 * x + 1] += (double)bf16_hi(kw[x]);
+        }
+        if (extrema && s < t.nvalid) {  // padded slots are not tokens
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            kmx[2 * x] = fmaxf(kmx[2 * x], bf16_lo(kw[x]));
+            kmx[2 * x + 1] = fmaxf(kmx[2 * x + 1], bf16_hi(kw[x]));
+            kmn[2 * x] = fminf(kmn[2 * x], bf16_lo(kw[x]));
+            kmn[2 * x + 1] = fminf(kmn[2 * x + 1], bf16_hi(kw[x]));
+          }
         }
       }
     }
@@ -171,9 +186,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
 
   if (!pool) return;
   // Exact sums: every partial sum of bf16 values of moderate range is exact
-  // in fp64, so the reduction order does not change the result.
+  // in fp64, so the reduction order does not change the result.  Extrema
+  // are exact in any order too.
   double* red = reinterpret_cast<double*>(smem);  // [kLayoutThreads][8]
+  float* redf = reinterpret_cast<float*>(smem);   // [kLayoutThreads][8]
+  const long dst_off = (bh * g.max_tiles + i) * D;
   for (int which = 0; which < 2; ++which) {
+    if (which == 1 && extrema) break;  // K gets its extrema below instead of its mean
 #pragma unroll
     for (int x = 0; x < 8; ++x) red[tid * 8 + x] = which ? sk[x] : sq[x];
     __syncthreads();
@@ -182,7 +201,24 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
       double s = 0.0;
       for (int r = 0; r < RPP; ++r) s += red[(r * P + pp) * 8 + xx];
       float* dst = which ? pooled_k : pooled_q;
-      dst[(bh * g.max_tiles + i) * D + tid] = (float)(s / (double)t.nvalid);
+      dst[dst_off + tid] = (float)(s / (double)t.nvalid);
+    }
+    __syncthreads();
+  }
+  if (!extrema) return;
+  for (int which = 0; which < 2; ++which) {
+    if (which == 1 && g.summ != VSA_SUMM_MINMAX) break;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) redf[tid * 8 + x] = which ? kmn[x] : kmx[x];
+    __syncthreads();
+    if (tid < D) {
+      const int pp = tid / 8, xx = tid % 8;
+      float m = redf[pp * 8 + xx];
+      for (int r = 1; r < RPP; ++r) {
+        const float v = redf[(r * P + pp) * 8 + xx];
+        m = which ? fminf(m, v) : fmaxf(m, v);
+      }
+      (which ? pooled_kmin : pooled_k)[dst_off + tid] = m;
     }
     __syncthreads();
   }
@@ -220,6 +256,7 @@ __device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int i
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float* __restrict__ pooled_q,
                                                              const float* __restrict__ pooled_k,
+                                                             const float* __restrict__ pooled_kmin,
                                                              const int* __restrict__ cand,
                                                              int* __restrict__ row_len,
                                                              int* __restrict__ col_idx) {
@@ -238,7 +275,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
   const int tid = threadIdx.x;
   const int D = g.d;
   const bool dense = (g.flags & VSA_DENSE) != 0;
-  for (int j = tid; j < n; j += kSelThreads) keep[j] = dense ? 1 : 0;
+  for (int j = tid; j < n; j += kSelThreads) keep[j] = (dense || j < g.sink) ? 1 : 0;
   __syncthreads();
 
   if (g.flags & VSA_WINDOW) {
@@ -279,7 +316,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         double acc = 0.0;
         // Fixed left-to-right order; each fp32 x fp32 product is exact in
         // fp64, so a fused multiply-add rounds exactly like mul-then-add.
-        for (int x = 0; x < D; ++x) acc = fma((double)qbar[x], (double)kr[x], acc);
+        if (g.summ == VSA_SUMM_MINMAX) {
+          const float* kn = pooled_kmin + (bh * g.max_tiles + j) * D;
+          for (int x = 0; x < D; ++x)
+            acc += fmax((double)qbar[x] * (double)kr[x], (double)qbar[x] * (double)kn[x]);
+        } else {
+          for (int x = 0; x < D; ++x) acc = fma((double)qbar[x], (double)kr[x], acc);
+        }
         sc[j] = acc * g.scale;
         sid[j] = j;
       } else {
@@ -359,10 +402,10 @@ hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uin
   const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
   if (g.d == 128)
     hipLaunchKernelGGL(layout_kernel<128>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
-                       w.vt, w.pooled_q, w.pooled_k, cand, pool ? 1 : 0);
+                       w.vt, w.pooled_q, w.pooled_k, w.pooled_kmin, cand, pool ? 1 : 0);
   else
     hipLaunchKernelGGL(layout_kernel<64>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
-                       w.vt, w.pooled_q, w.pooled_k, cand, pool ? 1 : 0);
+                       w.vt, w.pooled_q, w.pooled_k, w.pooled_kmin, cand, pool ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -380,7 +423,7 @@ hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hi
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
   const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, g, w.pooled_q, w.pooled_k, cand,
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, g, w.pooled_q, w.pooled_k, w.pooled_kmin, cand,
                      w.row_len, w.col_idx);
   return hipGetLastError();
 }

@@ -32,6 +32,8 @@ struct Geo {
   int win_mode;
   double topp;
   double scale;     // softmax scale
+  int summ;         // VSA_SUMM_* (dynamic masks)
+  int sink;         // leading key tiles kept for every query tile
   // fine-grained mask
   int fine_M, fine_G;
   long fine_keep;   // kept (group, key) pairs per head (target count)
@@ -71,6 +73,7 @@ struct Ws {
   uint16_t* vt;
   float* pooled_q;
   float* pooled_k;
+  float* pooled_kmin;
   int* row_len;
   int* col_idx;
   int* cand;
@@ -89,7 +92,9 @@ struct Ws {
 // Bytes of internal scratch the fine-grained mask needs (fine.hip).
 size_t fine_scratch_bytes(const Geo& g);
 
-// Kernel launchers (kernels.hip / sics.hip / fine.hip); return hipError_t.
+// Kernel launchers (layout_select.hip / attend.hip / sics.hip / fine.hip);
+// return hipError_t.  launch_layout's pool writes the block summaries of
+// dynamic masks (mean of Q, and mean / max / max+min of K per g.summ).
 hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, bool pool, hipStream_t s);
 hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s);

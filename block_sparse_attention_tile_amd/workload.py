@@ -2,7 +2,8 @@
 the C structs of the library.
 
 Attributes read: B, H, d, grid, tile, candidates, window, win_mode, topk,
-topk_frac, topp, fine_group, fine_keep.
+topk_frac, topp, fine_group, fine_keep, summarizer ("mean", "max" or
+"minmax"; optional, default mean), sink (optional, default 0).
 """
 from __future__ import annotations
 
@@ -29,7 +30,10 @@ def flags_of(wl):
 def plan_structs(wl):
     prob = _lib.make_problem(wl.B, wl.H, wl.d, wl.grid, wl.tile, wl.candidates)
     mode = _lib.VSA_WIN_CLAMP if wl.win_mode == "clamp" else _lib.VSA_WIN_TRUNCATE
+    summ = {"mean": _lib.VSA_SUMM_MEAN, "max": _lib.VSA_SUMM_MAX,
+            "minmax": _lib.VSA_SUMM_MINMAX}[getattr(wl, "summarizer", "mean")]
     pol = _lib.make_policy(flags_of(wl), win=wl.window or (1, 1, 1), win_mode=mode,
                            topk=wl.topk, topk_frac=wl.topk_frac, topp=wl.topp,
-                           fine_group=wl.fine_group, fine_keep=wl.fine_keep)
+                           fine_group=wl.fine_group, fine_keep=wl.fine_keep,
+                           summarizer=summ, sink=getattr(wl, "sink", 0))
     return prob, pol

@@ -62,8 +62,8 @@ extern "C" {
  * VSA_FINE        fine-grained M x 1 mask (M = fine_group), keep fraction
  *                 fine_keep of all (group, key) pairs per head.  Exclusive
  *                 with every other flag.
- * Window, Top-K and Top-P combine as a union.  Top-K over all key tiles,
- * then union with the window.                                             */
+ * Window, Top-K, Top-P and the sink (policy.sink) combine as a union.
+ * Top-K over all key tiles, then union with the window.                   */
 #define VSA_DENSE        0x01u
 #define VSA_WINDOW       0x02u
 #define VSA_TOPK         0x04u
@@ -71,6 +71,21 @@ extern "C" {
 #define VSA_TOPP         0x10u
 #define VSA_SICS_SELECT  0x20u
 #define VSA_FINE         0x40u
+
+/* Block summarizer and score estimator of dynamic (Top-K / Top-P) masks.
+ * The SPADE review page (referee report, minor comment 3; its ledger of
+ * axioms) names max, min and mean block summaries (the MEAN-, DSA- and
+ * DSA2-SPADE variants) but gives no expressions; the readings taken here,
+ * with q_i the mean of query tile i and every reduction per channel over
+ * the tile's valid tokens:
+ *   VSA_SUMM_MEAN    S_ij = scale * <q_i, mean_j(K)>
+ *   VSA_SUMM_MAX     S_ij = scale * <q_i, max_j(K)>
+ *   VSA_SUMM_MINMAX  S_ij = scale * sum_c max(q_ic max_j(K)_c, q_ic min_j(K)_c),
+ *                    an upper bound of scale * <q_i, k> over the keys k of
+ *                    tile j.                                               */
+#define VSA_SUMM_MEAN   0
+#define VSA_SUMM_MAX    1
+#define VSA_SUMM_MINMAX 2
 
 #define VSA_WIN_TRUNCATE 0  /* window cut at the grid edge */
 #define VSA_WIN_CLAMP    1  /* window shifted inward, keeps its full size */
@@ -96,6 +111,12 @@ typedef struct vsa_mask_policy {
   int32_t fine_group;     /* M for VSA_FINE, multiple of 16, >= 16 */
   double fine_keep;       /* kept fraction for VSA_FINE, in (0, 1] */
   double scale;           /* softmax scale; 0 selects 1/sqrt(d) */
+  int32_t summarizer;     /* VSA_SUMM_*; used by Top-K / Top-P only */
+  int32_t sink;           /* key tiles 0 .. sink-1 (raster tile order, the
+                             first frames) are kept for every query tile, an
+                             always-kept attention sink (SPADE review page,
+                             ledger free parameters: sink length, no value
+                             given); 0 = none.  Not with VSA_FINE. */
 } vsa_mask_policy;
 
 /* Opaque, immutable plan; safe to share between threads. */
@@ -124,8 +145,8 @@ typedef struct vsa_plan_info {
 #define VSA_WS_QT          0  /* bf16 [B*H][tiles*slots][d] tile-major Q */
 #define VSA_WS_KT          1  /* bf16 [B*H][tiles*slots][d] tile-major K */
 #define VSA_WS_VT          2  /* bf16 [B*H][tiles][d][slots] tile-major V, transposed per tile */
-#define VSA_WS_POOLED_Q    3  /* fp32 [B*H][max_tiles][d] */
-#define VSA_WS_POOLED_K    4  /* fp32 [B*H][max_tiles][d] */
+#define VSA_WS_POOLED_Q    3  /* fp32 [B*H][max_tiles][d] mean of Q */
+#define VSA_WS_POOLED_K    4  /* fp32 [B*H][max_tiles][d] mean (or, VSA_SUMM_MAX / MINMAX, maximum) of K */
 #define VSA_WS_ROW_LEN     5  /* int32 [B*H][max_tiles] kept tiles per row */
 #define VSA_WS_COL_IDX     6  /* int32 [B*H][max_tiles][row_cap] ascending */
 #define VSA_WS_CAND        7  /* int32 [B*H] chosen blocking */
@@ -139,7 +160,8 @@ typedef struct vsa_plan_info {
 #define VSA_WS_FINE_PTR   15  /* int32 [B*H][G+1] start of each group's keys */
 #define VSA_WS_FINE_SCORE 16  /* fp64 [B*H][G][N] group-key scores */
 #define VSA_WS_SCRATCH    17  /* internal */
-#define VSA_WS_NREGIONS   18
+#define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][max_tiles][d] per-channel K minimum (VSA_SUMM_MINMAX) */
+#define VSA_WS_NREGIONS   19
 
 /* ---- plan ---------------------------------------------------------------
  * Validates `prob` and `pol`, computes the tile geometry of every blocking,

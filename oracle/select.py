@@ -13,6 +13,17 @@ Follows, in order, the dynamic-mask steps of the SPADE review page:
 The kept pairs form the block mask M of the referee report's minor
 comment on Eq. (2): 0 on kept block pairs, -inf on pruned ones.
 
+Other summarizers (the SPADE review page names max, min and mean block
+summaries -- the DSA-, DSA2- and MEAN-SPADE variants, referee report minor
+comment 3 and the ledger's summarizer axiom -- without expressions; the
+readings taken here, every reduction per channel over the tile's valid
+tokens):
+  * "max":    S_ij = scale * <mean_i(Q), max_j(K)>;
+  * "minmax": S_ij = scale * sum_c max(q_ic max_j(K)_c, q_ic min_j(K)_c), an
+    upper bound of scale * <q_i, k> over the keys k of tile j.
+An attention sink (the ledger's free parameter "attention-sink length", no
+value given) keeps key tiles 0 .. sink-1 for every query tile.
+
 Arithmetic fixed here so that an independent implementation reaches the
 same integers:
   * pooled mean: exact sum of the bf16 values (asserted exact in fp64),
@@ -64,6 +75,43 @@ def pooled_means(x, members):
     return out
 
 
+def pooled_extrema(x, members):
+    """Per-channel max and min of each tile's valid tokens: x [N, d] ->
+    (max fp32 [nT, d], min fp32 [nT, d]); exact (the values are bf16)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    mx = np.zeros((len(members), x32.shape[1]), dtype=np.float32)
+    mn = np.zeros_like(mx)
+    for i, m in enumerate(members):
+        mx[i] = x32[m].max(axis=0)
+        mn[i] = x32[m].min(axis=0)
+    return mx, mn
+
+
+def tile_scores_bound(pq, kmax, kmin, scale):
+    """S[i, j] = scale * sum_c max(pq_ic * kmax_jc, pq_ic * kmin_jc): each
+    product exact in fp64, the sum left to right over c from 0."""
+    pq64 = np.asarray(pq, dtype=np.float64)
+    a64 = np.asarray(kmax, dtype=np.float64)
+    b64 = np.asarray(kmin, dtype=np.float64)
+    acc = np.zeros((pq64.shape[0], a64.shape[0]), dtype=np.float64)
+    for c in range(pq64.shape[1]):
+        acc = acc + np.maximum(np.outer(pq64[:, c], a64[:, c]), np.outer(pq64[:, c], b64[:, c]))
+    return acc * float(scale)
+
+
+def summarized_scores(q, k, members, scale, summarizer="mean"):
+    """Block scores of one head under a summarizer ("mean", "max", "minmax")."""
+    pq = pooled_means(q, members)
+    if summarizer == "mean":
+        return tile_scores(pq, pooled_means(k, members), scale)
+    kmax, kmin = pooled_extrema(k, members)
+    if summarizer == "max":
+        return tile_scores(pq, kmax, scale)
+    if summarizer == "minmax":
+        return tile_scores_bound(pq, kmax, kmin, scale)
+    raise ValueError(summarizer)
+
+
 def tile_scores(pq, pk, scale):
     """S[i, j] = scale * <pq_i, pk_j>, fixed left-to-right fp64 order."""
     pq64 = np.asarray(pq, dtype=np.float64)
@@ -108,8 +156,8 @@ def topp(row, p):
     return sorted(int(j) for j in order[:m + 1]), float(margin)
 
 
-def select_rows(S, ntiles, window=None, win_mode="truncate", k=0, p=0.0):
-    """Per query tile: window(i) U TopK(i) U TopP(i), sorted ascending.
+def select_rows(S, ntiles, window=None, win_mode="truncate", k=0, p=0.0, sink=0):
+    """Per query tile: window(i) U TopK(i) U TopP(i) U sink, sorted ascending.
 
     S is the [nT, nT] score matrix (may be None when only the window is
     used).  Returns (rows, margins) where margins holds the Top-P margin
@@ -118,7 +166,7 @@ def select_rows(S, ntiles, window=None, win_mode="truncate", k=0, p=0.0):
     nT = int(np.prod(ntiles))
     rows, margins = [], []
     for i in range(nT):
-        keep = set()
+        keep = set(range(min(sink, nT)))
         if window is not None:
             keep.update(geometry.window(i, ntiles, window, win_mode))
         margin = math.inf

@@ -26,6 +26,8 @@ class Workload:
     topp: float = 0.0
     fine_group: int = 0
     fine_keep: float = 0.0
+    summarizer: str = "mean"              # block summary of K: "mean", "max", "minmax"
+    sink: int = 0                         # leading key tiles always kept
     ell: Tuple[float, float, float] = (2.0, 2.0, 2.0)
     ell_alt: Optional[Tuple[float, float, float]] = None  # odd heads
     note: str = ""

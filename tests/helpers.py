@@ -22,13 +22,11 @@ def oracle_tile_rows(wl, q_h, k_h, tile):
         K = min(select.frac_count(wl.topk_frac, nT), nT)
     S = None
     if K or wl.topp:
-        pq = select.pooled_means(q_h, mem)
-        pk = select.pooled_means(k_h, mem)
-        S = select.tile_scores(pq, pk, select.default_scale(wl.d))
+        S = select.summarized_scores(q_h, k_h, mem, select.default_scale(wl.d), wl.summarizer)
     if wl.window is None and not K and not wl.topp:
         return [list(range(nT))] * nT, [np.inf] * nT, mem
     rows, margins = select.select_rows(S, nt, window=wl.window, win_mode=wl.win_mode,
-                                       k=K, p=wl.topp)
+                                       k=K, p=wl.topp, sink=wl.sink)
     return rows, margins, mem
 
 

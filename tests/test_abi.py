@@ -95,6 +95,23 @@ def test_ragged_static_flops():
     assert info.static_flops == pytest.approx(fl, rel=1e-12)
 
 
+def test_static_window_with_sink_counts_the_union():
+    wl = CONFIGS["hunyuan"]
+    prob, _ = structs_of(wl)
+    pol = vsa.make_policy(vsa.VSA_WINDOW, win=wl.window, sink=3)
+    info = vsa.vsa_plan_get_info(vsa.vsa_plan(prob, pol))
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    nt = geometry.tile_counts(wl.grid, wl.tile)
+    pairs, fl = 0, 0.0
+    for i in range(len(mem)):
+        row = set(geometry.window(i, nt, wl.window, "truncate")) | {0, 1, 2}
+        pairs += len(row)
+        fl += sum(len(mem[i]) * len(mem[j]) for j in row)
+    assert info.static_pairs == pairs
+    assert info.static_flops == pytest.approx(fl * 4 * wl.d * wl.B * wl.H, rel=1e-12)
+    assert info.row_cap == 48
+
+
 def _err(prob, pol):
     with pytest.raises(vsa.VsaError) as e:
         vsa.vsa_plan(prob, pol)
@@ -120,6 +137,10 @@ def test_plan_errors():
     assert _err(ok, vsa.make_policy(vsa.VSA_SICS_SELECT | vsa.VSA_TOPK, topk=2)) \
         == vsa._lib.VSA_ERR_INVALID_ARG          # n_cand = 0
     assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), scale=-1.0)) \
+        == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_TOPK, topk=2, summarizer=3)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), sink=-1)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_FINE, fine_group=64, fine_keep=0.1, sink=1)) \
         == vsa._lib.VSA_ERR_INVALID_ARG
     with pytest.raises(vsa.VsaError):
         vsa.vsa_plan(None, win) if False else _lib._check(vsa.lib().vsa_plan(None, None, None))

@@ -34,6 +34,13 @@ SMALL = {
     "dense_b2": Workload("dense_b2", 2, 2, 64, (3, 5, 6), (1, 5, 6)),
     # Top-K only (scores decide everything), d=128, 112-token tiles
     "topk_only": Workload("topk_only", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3),
+    # max summarizer of K (scores against per-channel key maxima)
+    "topk_max": Workload("topk_max", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3, summarizer="max"),
+    # max/min bound estimator + attention sink + window, ragged tiles, d=64
+    "topp_minmax_sink": Workload("topp_minmax_sink", 1, 3, 64, (5, 7, 9), (2, 3, 4), window=(3, 3, 3),
+                                 topp=0.9, summarizer="minmax", sink=2),
+    # static window + sink (the plan's static counts include the sink)
+    "window_sink": Workload("window_sink", 1, 2, 128, (12, 16, 24), (6, 8, 8), window=(1, 1, 3), sink=4),
 }
 
 
@@ -89,11 +96,19 @@ def test_pooled_means_bit_exact(name):
     nT = len(mem)
     pq = plan.region(_lib.VSA_WS_POOLED_Q, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
     pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
+    if wl.summarizer == "minmax":
+        pkn = plan.region(_lib.VSA_WS_POOLED_KMIN, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
     qn, kn = q.float().cpu().numpy(), k.float().cpu().numpy()
     for b in range(wl.B):
         for h in range(wl.H):
             assert np.array_equal(pq[b * wl.H + h], select.pooled_means(qn[b, h], mem))
-            assert np.array_equal(pk[b * wl.H + h], select.pooled_means(kn[b, h], mem))
+            if wl.summarizer == "mean":
+                assert np.array_equal(pk[b * wl.H + h], select.pooled_means(kn[b, h], mem))
+            else:
+                kmax, kmin = select.pooled_extrema(kn[b, h], mem)
+                assert np.array_equal(pk[b * wl.H + h], kmax)
+                if wl.summarizer == "minmax":
+                    assert np.array_equal(pkn[b * wl.H + h], kmin)
 
 
 @pytest.mark.parametrize("name", list(SMALL))

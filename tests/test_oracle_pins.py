@@ -180,6 +180,62 @@ def test_pooled_exactness_guard_fires():
         select.pooled_means(x, [np.arange(4)])
 
 
+# ------------------------------------------------- max / min summarizers
+
+def test_pooled_extrema_match_torch_amax_amin():
+    grid, tile = (4, 8, 8), (2, 4, 4)
+    x = _bf16((256, 64), 13)
+    mx, mn = select.pooled_extrema(x, geometry.tile_members(grid, tile))
+    ref = torch.from_numpy(x).view(2, 2, 2, 4, 2, 4, 64).permute(0, 2, 4, 1, 3, 5, 6).reshape(8, 32, 64)
+    assert np.array_equal(mx, ref.amax(dim=1).numpy())
+    assert np.array_equal(mn, ref.amin(dim=1).numpy())
+
+
+def test_pooled_extrema_ragged_tile_uses_valid_tokens():
+    grid, tile = (1, 1, 52), (1, 1, 8)          # last tile has 4 tokens
+    x = _bf16((52, 16), 14)
+    mx, mn = select.pooled_extrema(x, geometry.tile_members(grid, tile))
+    assert np.array_equal(mx[-1], x[48:52].max(0)) and np.array_equal(mn[-1], x[48:52].min(0))
+
+
+def test_minmax_score_bounds_every_key_of_the_tile():
+    grid, tile = (2, 6, 6), (1, 3, 3)
+    q, k = _bf16((72, 32), 15), _bf16((72, 32), 16)
+    mem = geometry.tile_members(grid, tile)
+    S = select.summarized_scores(q, k, mem, 0.25, "minmax")
+    pq = select.pooled_means(q, mem).astype(np.float64)
+    for j, m in enumerate(mem):
+        exact = (pq @ k[m].astype(np.float64).T).max(axis=1) * 0.25   # best key of tile j
+        assert np.all(S[:, j] >= exact - 1e-12)
+
+
+def test_summarizers_coincide_on_one_token_tiles():
+    grid, tile = (1, 3, 4), (1, 1, 1)
+    q, k = _bf16((12, 16), 17), _bf16((12, 16), 18)
+    mem = geometry.tile_members(grid, tile)
+    ref = (q.astype(np.float64) @ k.astype(np.float64).T) * 0.5         # closed form
+    for summ in ("mean", "max", "minmax"):
+        assert np.allclose(select.summarized_scores(q, k, mem, 0.5, summ), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_max_summarizer_scores_against_the_key_maxima():
+    grid, tile = (4, 8, 8), (2, 4, 4)
+    q, k = _bf16((256, 64), 19), _bf16((256, 64), 20)
+    mem = geometry.tile_members(grid, tile)
+    kmax = torch.from_numpy(k).view(2, 2, 2, 4, 2, 4, 64).permute(0, 2, 4, 1, 3, 5, 6).reshape(8, 32, 64).amax(1)
+    ref = torch.from_numpy(select.pooled_means(q, mem)).double() @ kmax.double().T * 0.125
+    assert np.allclose(select.summarized_scores(q, k, mem, 0.125, "max"), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sink_is_kept_in_every_row():
+    S = np.arange(64, dtype=np.float64).reshape(8, 8)          # col 7 best
+    rows, _ = select.select_rows(S, (2, 2, 2), window=(1, 1, 1), k=1, sink=2)
+    for i, r in enumerate(rows):
+        assert r == sorted({0, 1, i, 7})
+    assert select.select_rows(S, (2, 2, 2), window=(1, 1, 1), sink=0)[0] == [[i] for i in range(8)]
+    assert all(r == list(range(8)) for r in select.select_rows(S, (2, 2, 2), window=(1, 1, 1), sink=99)[0])
+
+
 # ------------------------------------------------------------- tile scores
 
 def test_scores_match_fp64_matmul():
