@@ -19,5 +19,6 @@ Modules:
   sics      - SICS tile-coherence score and candidate blocking choice
   fine      - M x 1 fine-grained group mask
   attention - masked softmax attention (dense definition + block-sparse)
+  fp8       - E4M3 quantization and the FP8 attention path
 """
-from . import geometry, layout, select, sics, fine, attention  # noqa: F401
+from . import geometry, layout, select, sics, fine, attention, fp8  # noqa: F401
