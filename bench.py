@@ -24,9 +24,11 @@ sys.path.insert(0, ROOT)
 METRIC = ("ms/attention call + effective TFLOP/s on retained blocks, "
           "HunyuanVideo-720p shape")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ATTN_SOURCES = ["block_sparse_attention_tile_amd/csrc/attend.hip",
-                "block_sparse_attention_tile_amd/csrc/attn_core.h"]
+                "block_sparse_attention_tile_amd/csrc/attn_core.h",
+                "block_sparse_attention_tile_amd/csrc/attn_core_f8.h"]
 
 
 def _src_hash(paths):
@@ -106,6 +108,8 @@ def main():
     ap.add_argument("--summarizer", choices=["mean", "max", "minmax"], default=None,
                     help="override the workload's block summarizer (dynamic masks)")
     ap.add_argument("--sink", type=int, default=None, help="override the workload's sink tiles")
+    ap.add_argument("--compute", choices=["bf16", "fp8"], default=None,
+                    help="override the attention arithmetic (fp8 = E4M3 Q, K, V and probabilities)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -124,6 +128,9 @@ def main():
         wl = wl.with_(summarizer=args.summarizer)
     if args.sink is not None:
         wl = wl.with_(sink=args.sink)
+    if args.compute is not None:
+        wl = wl.with_(compute=args.compute)
+    f8 = wl.compute == "fp8"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
@@ -184,15 +191,17 @@ def main():
     BH = wl.B * wl.H
     # read Q, K, V + write the tile-major copies (no layout stage for the
     # fine-grained mask, which reads the raster tensors directly)
-    bytes_layout = 0.0 if wl.fine_group else 6.0 * BH * wl.N * wl.d * 2
+    # (E4M3: one more read of Q, K, V for the per-head maxima, 1-byte writes)
+    bytes_layout = 0.0 if wl.fine_group else BH * wl.N * wl.d * (15.0 if f8 else 12.0)
     attn_tflops = flops / (ms_attend * 1e-3) / 1e12
-    traffic = _traffic("attend", wl.name)
-    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+    peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
+    traffic = _traffic("attend_fp8" if f8 else "attend", wl.name)
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                 "traffic": traffic}
 
     cpu = None
-    if args.cpu_budget > 0 and not wl.fine_group and not wl.candidates:
+    if args.cpu_budget > 0 and not wl.fine_group and not wl.candidates and not f8:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = _cpu_baseline(wl, q, k, v, plan, args.cpu_budget)
 
@@ -208,7 +217,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if f8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} N={wl.N} "
                                f"({wl.grid[0]}x{wl.grid[1]}x{wl.grid[2]}) d={wl.d} "

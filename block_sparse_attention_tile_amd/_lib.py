@@ -32,11 +32,14 @@ VSA_MAX_CAND = 4
 VSA_SUMM_MEAN = 0
 VSA_SUMM_MAX = 1
 VSA_SUMM_MINMAX = 2
+VSA_COMPUTE_BF16 = 0
+VSA_COMPUTE_FP8 = 1
 
 (VSA_WS_QT, VSA_WS_KT, VSA_WS_VT, VSA_WS_POOLED_Q, VSA_WS_POOLED_K, VSA_WS_ROW_LEN,
  VSA_WS_COL_IDX, VSA_WS_CAND, VSA_WS_CAND_SCORE, VSA_WS_TILE_SICS, VSA_WS_ATOMS,
  VSA_WS_FINE_QBAR, VSA_WS_FINE_TAU, VSA_WS_FINE_COUNT, VSA_WS_FINE_IDX, VSA_WS_FINE_PTR,
- VSA_WS_FINE_SCORE, VSA_WS_SCRATCH, VSA_WS_POOLED_KMIN, VSA_WS_NREGIONS) = range(20)
+ VSA_WS_FINE_SCORE, VSA_WS_SCRATCH, VSA_WS_POOLED_KMIN, VSA_WS_F8_EXP, VSA_WS_F8_AMAX,
+ VSA_WS_NREGIONS) = range(22)
 
 EXPORTED = [
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_workspace_bytes",
@@ -57,7 +60,7 @@ class vsa_mask_policy(C.Structure):
     _fields_ = [("flags", C.c_uint32), ("win", C.c_int32 * 3), ("win_mode", C.c_int32),
                 ("topk", C.c_int32), ("topk_frac", C.c_double), ("topp", C.c_double),
                 ("fine_group", C.c_int32), ("fine_keep", C.c_double), ("scale", C.c_double),
-                ("summarizer", C.c_int32), ("sink", C.c_int32)]
+                ("summarizer", C.c_int32), ("sink", C.c_int32), ("compute", C.c_int32)]
 
 
 class vsa_plan_info(C.Structure):
@@ -141,7 +144,8 @@ def make_problem(B, H, d, grid, tile, candidates=()):
 
 
 def make_policy(flags, win=(1, 1, 1), win_mode=VSA_WIN_TRUNCATE, topk=0, topk_frac=0.0,
-                topp=0.0, fine_group=0, fine_keep=0.0, scale=0.0, summarizer=VSA_SUMM_MEAN, sink=0):
+                topp=0.0, fine_group=0, fine_keep=0.0, scale=0.0, summarizer=VSA_SUMM_MEAN, sink=0,
+                compute=VSA_COMPUTE_BF16):
     p = vsa_mask_policy()
     p.flags = flags
     p.win[:] = list(win)
@@ -154,6 +158,7 @@ def make_policy(flags, win=(1, 1, 1), win_mode=VSA_WIN_TRUNCATE, topk=0, topk_fr
     p.scale = scale
     p.summarizer = summarizer
     p.sink = sink
+    p.compute = compute
     return p
 
 

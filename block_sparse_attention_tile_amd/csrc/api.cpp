@@ -114,6 +114,8 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.fine_ptr = (int*)at(VSA_WS_FINE_PTR);
   w.fine_score = (double*)at(VSA_WS_FINE_SCORE);
   w.scratch = (unsigned char*)at(VSA_WS_SCRATCH);
+  w.f8_exp = (int*)at(VSA_WS_F8_EXP);
+  w.f8_amax = (uint32_t*)at(VSA_WS_F8_AMAX);
   return w;
 }
 
@@ -177,6 +179,12 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     return fail(VSA_ERR_INVALID_ARG, "the tile sink does not apply to VSA_FINE");
   g.summ = po->summarizer;
   g.sink = po->sink;
+  if (po->compute != VSA_COMPUTE_BF16 && po->compute != VSA_COMPUTE_FP8)
+    return fail(VSA_ERR_INVALID_ARG, "compute must be VSA_COMPUTE_BF16 or VSA_COMPUTE_FP8 (got %d)",
+                po->compute);
+  if (po->compute == VSA_COMPUTE_FP8 && (f & VSA_FINE))
+    return fail(VSA_ERR_UNSUPPORTED, "VSA_COMPUTE_FP8 is built for tile masks only, not VSA_FINE");
+  g.f8 = po->compute == VSA_COMPUTE_FP8 ? 1 : 0;
 
   if (f & VSA_FINE) {
     int M = po->fine_group;
@@ -319,6 +327,10 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     sz[VSA_WS_ROW_LEN] = (size_t)BH * g.max_tiles * 4;
     sz[VSA_WS_COL_IDX] = (size_t)BH * g.max_tiles * g.row_cap * 4;
     sz[VSA_WS_CAND] = (size_t)BH * 4;
+    if (g.f8) {
+      sz[VSA_WS_F8_EXP] = (size_t)BH * 3 * 4;
+      sz[VSA_WS_F8_AMAX] = (size_t)BH * 3 * vsa::kAmaxParts * 4;
+    }
     if (f & VSA_SICS_SELECT) {
       sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;
       sz[VSA_WS_TILE_SICS] = (size_t)BH * g.nb * 2 * g.max_tiles * 4;
@@ -357,6 +369,10 @@ int enqueue_layout(const vsa_plan_t* p, const void* q, const void* k, const void
     if (e != hipSuccess) return hip_fail(e, "SICS kernels");
   }
   bool pool = mask && (g.flags & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) != 0;
+  if (g.f8) {  // the E4M3 scales need every head's max |x| before the layout
+    e = vsa::launch_amax(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s);
+    if (e != hipSuccess) return hip_fail(e, "max-abs kernel");
+  }
   e = vsa::launch_layout(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pool, s);
   if (e != hipSuccess) return hip_fail(e, "layout kernel");
   return VSA_OK;
@@ -525,6 +541,7 @@ int vsa_untile(const vsa_plan_t* p, int which, const void* ws, size_t ws_bytes, 
   int st = check_exec(p, ws, ws_bytes);
   if (st) return st;
   if (p->geo.flags & VSA_FINE) return fail(VSA_ERR_UNSUPPORTED, "no tiled layout under VSA_FINE");
+  if (p->geo.f8) return fail(VSA_ERR_UNSUPPORTED, "the tiled layout holds E4M3 under VSA_COMPUTE_FP8");
   if (which != 0 && which != 1) return fail(VSA_ERR_INVALID_ARG, "which must be 0 (Q) or 1 (K)");
   if ((st = check_tensor(out, "out"))) return st;
   if ((st = check_device())) return st;

@@ -18,7 +18,10 @@
 //    the ring is multiplied per barrier while the other half is in flight.
 //  * The kept-tile list is copied to LDS first, so the loop issues no other
 //    global loads that would drain the queue.
-//  * The MFMA / online-softmax math per 32-key block is in attn_core.h.
+//  * The MFMA / online-softmax math per 32-key block is in attn_core.h
+//    (bf16) and attn_core_f8.h (E4M3, VSA_COMPUTE_FP8: Sparse VideoGen
+//    verdict page, optional FP8 attention; per-head power-of-two scales
+//    from the layout stage).
 //  * The epilogue writes O straight to the raster layout (the inverse
 //    permutation is fused here), skipping padded query slots.
 //  * Workgroups are mapped XCD-major: consecutive work items (same head,
@@ -27,13 +30,33 @@
 #include <hip/hip_runtime.h>
 
 #include "attn_core.h"
+#include "attn_core_f8.h"
 #include "vsa_internal.h"
 
 namespace vsa {
 namespace {
 
 using core::kKC;
-using core::Lds;
+static_assert(core::kKC == core8::kKC, "one chunk size");
+
+// The two arithmetic variants of the kernel: element type of the staged
+// tiles, LDS stage layout and per-wave core.
+template <int D_>
+struct Bf16Core {
+  static constexpr int D = D_;
+  static constexpr bool kF8 = false;
+  using T = uint16_t;
+  using L = core::Lds<D>;
+  using WS = core::WaveState<D>;
+};
+template <int D_>
+struct F8Core {
+  static constexpr int D = D_;
+  static constexpr bool kF8 = true;
+  using T = uint8_t;
+  using L = core8::Lds<D>;
+  using WS = core8::WaveState<D>;
+};
 
 constexpr int kMaxWaves = 12;
 constexpr int kNumXcd = 8;
@@ -110,15 +133,20 @@ struct ChunkIter {
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
 // Each wave instruction moves 64 lanes x 16 B into 1 KB of contiguous LDS;
 // the lane's global source is picked so that LDS ends up in the padded,
-// lane-ordered layout of Lds<D> (a padding unit re-reads its row's last data
-// unit).  The NI instructions of a chunk are dealt round-robin over the
+// lane-ordered layout of the stage (a padding unit re-reads its row's last
+// data unit).  The NI instructions of a chunk are dealt round-robin over the
 // waves.  A 32-key chunk clamps the source rows / key columns past 32 to the
-// last valid ones: every access stays inside the tile and the extra LDS slots
-// are never read.
-template <int D, int NW>
+// last valid ones: every access stays inside the tile, and every LDS byte
+// of the stage holds tile data (slots the math does not use are multiplied
+// by zero probabilities, never by stale memory).
+template <class C, int NW>
 struct ChunkLoader {
-  static constexpr int KU = kKC * (Lds<D>::KC16 + 1);  // 16-byte units of the K part
-  static constexpr int VU = D * (Lds<D>::VC16 + 1);    // and of the V^T part
+  static constexpr int D = C::D;
+  using L = typename C::L;
+  using T = typename C::T;
+  static constexpr int E = 16 / (int)sizeof(T);        // elements per 16-byte unit
+  static constexpr int KU = kKC * (L::KC16 + 1);       // 16-byte units of the K part
+  static constexpr int VU = D * (L::VC16 + 1);         // and of the V^T part
   static constexpr int KI = KU / 64;                   // K instructions (1 KB each)
   static constexpr int VI = VU / 64;                   // V^T instructions
   static constexpr int NI = KI + VI;
@@ -140,15 +168,14 @@ struct ChunkLoader {
       const int ins = ins_of(wave, x);
       const int u = ins * 64 + lane;
       if (ins < KI) {
-        const int p = u / (Lds<D>::KC16 + 1);                   // physical row
-        const int c = min(u % (Lds<D>::KC16 + 1), Lds<D>::KC16 - 1);
-        const int key = (p & ~31) | core::key_perm(p & 31);
-        off_full[x] = key * D + c * 8;
+        const int p = u / (L::KC16 + 1);                   // physical row
+        const int c = min(u % (L::KC16 + 1), L::KC16 - 1);
+        off_full[x] = L::key_of_row(p) * D + c * E;
       } else {
         const int v = u - KU;
-        const int d = v / (Lds<D>::VC16 + 1);
-        const int c = min(v % (Lds<D>::VC16 + 1), Lds<D>::VC16 - 1);
-        off_full[x] = d * slots + c * 8;
+        const int d = v / (L::VC16 + 1);
+        const int c = min(v % (L::VC16 + 1), L::VC16 - 1);
+        off_full[x] = d * slots + c * E;
       }
     }
   }
@@ -157,21 +184,22 @@ struct ChunkLoader {
   // key columns past 31 are clamped to the last valid ones (derived from the
   // 64-key offset: K rows are D apart, the V^T column unit is recomputed).
   __device__ __forceinline__ int off_half(int x) const {
+    constexpr int HU = L::VC16 / 2;  // data units of 32 keys
     const int ins = ins_of(wave, x);
     if (ins < KI) return min(off_full[x], 31 * D + (off_full[x] & (D - 1)));
-    const int c = min((ins * 64 + lane - KU) % (Lds<D>::VC16 + 1), Lds<D>::VC16 - 1);
-    return off_full[x] - max(c - 3, 0) * 8;
+    const int c = min((ins * 64 + lane - KU) % (L::VC16 + 1), L::VC16 - 1);
+    return off_full[x] - max(c - (HU - 1), 0) * E;
   }
 
-  __device__ __forceinline__ void issue(uint16_t* stage, const uint16_t* __restrict__ kbase,
-                                        const uint16_t* __restrict__ vbase, bool half) const {
+  __device__ __forceinline__ void issue(T* stage, const T* __restrict__ kbase,
+                                        const T* __restrict__ vbase, bool half) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
-      const uint16_t* base = ins < KI ? kbase : vbase;
+      const T* base = ins < KI ? kbase : vbase;
       __builtin_amdgcn_global_load_lds(base + (half ? off_half(x) : off_full[x]),
-                                       (lds_ptr_t)(stage + ins * 512), 16, 0, 0);
+                                       (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))), 16, 0, 0);
     }
   }
 };
@@ -188,13 +216,18 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 // so two small workgroups can share a CU.
 constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
-template <int D, int NW, int STAGES>
+template <class C, int NW, int STAGES>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
-    Geo g, int blocking, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ kt,
-    const uint16_t* __restrict__ vt, const int* __restrict__ row_len, const int* __restrict__ col_idx,
-    const int* __restrict__ cand, uint16_t* __restrict__ o, int nsb, int n_items) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  using Loader = ChunkLoader<D, NW>;
+    Geo g, int blocking, const typename C::T* __restrict__ qt, const typename C::T* __restrict__ kt,
+    const typename C::T* __restrict__ vt, const int* __restrict__ row_len,
+    const int* __restrict__ col_idx, const int* __restrict__ cand, const int* __restrict__ f8_exp,
+    uint16_t* __restrict__ o, int nsb, int n_items) {
+  constexpr int D = C::D;
+  using T = typename C::T;
+  using Stage = typename C::L;
+  extern __shared__ __align__(16) unsigned char lds_bytes[];
+  T* const lds = reinterpret_cast<T*>(lds_bytes);
+  using Loader = ChunkLoader<C, NW>;
 
   // XCD-major mapping of workgroups to work items.
   const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
@@ -220,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   const long head_tm = bh * g.tok_cap * D;
 
   // kept-tile list -> LDS (after the K/V stages)
-  int* cols = reinterpret_cast<int*>(lds + STAGES * Lds<D>::STAGE);
+  int* cols = reinterpret_cast<int*>(lds + STAGES * Stage::STAGE);
   // (row length and tile indices clamped: a selection that was never
   // written still keeps every access in bounds)
   const int L = min(max(row_len[bh * g.max_tiles + i], 0), g.row_cap);
@@ -230,9 +263,19 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     cols[e] = (tile_nvalid(g, b, j) << kTileBits) | j;
   }
 
-  core::WaveState<D> ws;
+  typename C::WS ws;
   if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
-  const float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
+  float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
+  float oscale = 1.f;
+  if constexpr (C::kF8) {
+    // scores carry 2^(e_q + e_k), values 2^e_v (clamped like the layout's
+    // exponents, so an unwritten workspace still gives finite factors)
+    const int eq = min(max(f8_exp[bh * 3 + 0], -32), 32);
+    const int ek = min(max(f8_exp[bh * 3 + 1], -32), 32);
+    const int ev = min(max(f8_exp[bh * 3 + 2], -32), 32);
+    c2 = __builtin_amdgcn_ldexpf(c2, -(eq + ek));
+    oscale = __builtin_amdgcn_ldexpf(1.f, -ev);
+  }
   Loader ldr;
   ldr.init(wave, lane, slots);
   __syncthreads();  // cols visible
@@ -244,8 +287,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   for (int m = 32; m >= 1; m >>= 1) total += __shfl_xor(total, m);
   total = __builtin_amdgcn_readfirstlane(total);
 
-  const uint16_t* kt_head = kt + head_tm;
-  const uint16_t* vt_head = vt + head_tm;
+  const T* kt_head = kt + head_tm;
+  const T* vt_head = vt + head_tm;
   ChunkIter ld_it, cur;
   ld_it.start(cols, L);
   cur = ld_it;
@@ -259,7 +302,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 #pragma unroll
   for (int s = 0; s < CPB; ++s) {
     if (s < total) {
-      ldr.issue(lds + s * Lds<D>::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+      ldr.issue(lds + s * Stage::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                 vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
       ld_it.next(cols, L);
     }
@@ -270,7 +313,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     for (int u = 0; u < CPB; ++u) {
       const int nc = c + CPB + u;
       if (nc < total) {
-        ldr.issue(lds + (nc % STAGES) * Lds<D>::STAGE,
+        ldr.issue(lds + (nc % STAGES) * Stage::STAGE,
                   kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                   vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
         ld_it.next(cols, L);
@@ -279,8 +322,8 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 #pragma unroll
     for (int u = 0; u < CPB; ++u) {
       if (c + u < total) {
-        const uint16_t* lk = lds + ((c + u) % STAGES) * Lds<D>::STAGE;
-        if (active) ws.chunk(lk, lk + Lds<D>::KE, cur.keys(), c2, col, hi);
+        const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
+        if (active) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
         cur.next(cols, L);
       }
     }
@@ -290,49 +333,59 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   const TileInfo ti = tinfo(g, b, i);
   const int qs = qrow + col;  // slot of this lane's query
   const bool valid = qs < ti.nvalid;
-  ws.store(o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D, hi, valid);
+  uint16_t* const orow = o + (bh * (long)g.N + (valid ? token_of(g, b, ti, qs) : 0)) * D;
+  if constexpr (C::kF8)
+    ws.store(orow, hi, valid, oscale);
+  else
+    ws.store(orow, hi, valid);
 }
 
 // Explicit instantiations of every kernel the launchers can pick.  (With
 // several implicit instantiations sharing a wave count, taking a kernel's
 // host-side address for hipFuncSetAttribute has left some host stubs
 // undefined in the shared library.)
-#define VSA_ATTEND_INST(D, NW, ST)                                                                   \
-  template __global__ void attend_kernel<D, NW, ST>(Geo, int, const uint16_t*, const uint16_t*,     \
-                                                    const uint16_t*, const int*, const int*,         \
+#define VSA_ATTEND_INST(C, NW, ST)                                                             \
+  template __global__ void attend_kernel<C, NW, ST>(Geo, int, const typename C::T*,           \
+                                                    const typename C::T*, const typename C::T*, \
+                                                    const int*, const int*, const int*,        \
                                                     const int*, uint16_t*, int, int);
-#define VSA_ATTEND_INST_D(D)                                                               \
-  VSA_ATTEND_INST(D, 1, 2) VSA_ATTEND_INST(D, 2, 2) VSA_ATTEND_INST(D, 3, 2)    \
-  VSA_ATTEND_INST(D, 4, 2) VSA_ATTEND_INST(D, 5, 2) VSA_ATTEND_INST(D, 6, 2)    \
-  VSA_ATTEND_INST(D, 7, 2) VSA_ATTEND_INST(D, 8, 2) VSA_ATTEND_INST(D, 9, 4)    \
-  VSA_ATTEND_INST(D, 10, 4) VSA_ATTEND_INST(D, 11, 4) VSA_ATTEND_INST(D, 12, 4)
-VSA_ATTEND_INST_D(128)
-VSA_ATTEND_INST_D(64)
-#undef VSA_ATTEND_INST_D
+#define VSA_ATTEND_INST_C(C)                                                               \
+  VSA_ATTEND_INST(C, 1, 2) VSA_ATTEND_INST(C, 2, 2) VSA_ATTEND_INST(C, 3, 2)    \
+  VSA_ATTEND_INST(C, 4, 2) VSA_ATTEND_INST(C, 5, 2) VSA_ATTEND_INST(C, 6, 2)    \
+  VSA_ATTEND_INST(C, 7, 2) VSA_ATTEND_INST(C, 8, 2) VSA_ATTEND_INST(C, 9, 4)    \
+  VSA_ATTEND_INST(C, 10, 4) VSA_ATTEND_INST(C, 11, 4) VSA_ATTEND_INST(C, 12, 4)
+VSA_ATTEND_INST_C(Bf16Core<128>)
+VSA_ATTEND_INST_C(Bf16Core<64>)
+VSA_ATTEND_INST_C(F8Core<128>)
+VSA_ATTEND_INST_C(F8Core<64>)
+#undef VSA_ATTEND_INST_C
 #undef VSA_ATTEND_INST
 
-template <int D, int NW, int STAGES>
+template <class C, int NW, int STAGES>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
+  using T = typename C::T;
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
   const int nsb = (slabs + NW - 1) / NW;
   const long items = (long)g.B * g.H * g.max_tiles * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
-  const size_t shmem = (size_t)STAGES * Lds<D>::STAGE * sizeof(uint16_t) + (size_t)g.row_cap * 4;
+  const size_t shmem = (size_t)STAGES * C::L::STAGE * sizeof(T) + (size_t)g.row_cap * 4;
   static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
   if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, NW, STAGES>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<D, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
-                     g, blocking, w.qt, w.kt, w.vt, w.row_len, w.col_idx, cand, o, nsb, (int)items);
+  hipLaunchKernelGGL((attend_kernel<C, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+                     g, blocking, reinterpret_cast<const T*>(w.qt), reinterpret_cast<const T*>(w.kt),
+                     reinterpret_cast<const T*>(w.vt), w.row_len, w.col_idx, cand, w.f8_exp, o, nsb,
+                     (int)items);
   return hipGetLastError();
 }
 
-template <int D>
+template <class C>
 hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                     hipStream_t s) {
   // Waves per workgroup: the tile's 32-row slabs split into as few balanced
@@ -343,18 +396,18 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
   const int groups = (slabs + kMaxWaves - 1) / kMaxWaves;
   const int nw = (slabs + groups - 1) / groups;
   switch (nw) {
-    case 1: return launch_one<D, 1, 2>(g, w, blocking, cand, o, s);
-    case 2: return launch_one<D, 2, 2>(g, w, blocking, cand, o, s);
-    case 3: return launch_one<D, 3, 2>(g, w, blocking, cand, o, s);
-    case 4: return launch_one<D, 4, 2>(g, w, blocking, cand, o, s);
-    case 5: return launch_one<D, 5, 2>(g, w, blocking, cand, o, s);
-    case 6: return launch_one<D, 6, 2>(g, w, blocking, cand, o, s);
-    case 7: return launch_one<D, 7, 2>(g, w, blocking, cand, o, s);
-    case 8: return launch_one<D, 8, 2>(g, w, blocking, cand, o, s);
-    case 9: return launch_one<D, 9, 4>(g, w, blocking, cand, o, s);
-    case 10: return launch_one<D, 10, 4>(g, w, blocking, cand, o, s);
-    case 11: return launch_one<D, 11, 4>(g, w, blocking, cand, o, s);
-    default: return launch_one<D, 12, 4>(g, w, blocking, cand, o, s);
+    case 1: return launch_one<C, 1, 2>(g, w, blocking, cand, o, s);
+    case 2: return launch_one<C, 2, 2>(g, w, blocking, cand, o, s);
+    case 3: return launch_one<C, 3, 2>(g, w, blocking, cand, o, s);
+    case 4: return launch_one<C, 4, 2>(g, w, blocking, cand, o, s);
+    case 5: return launch_one<C, 5, 2>(g, w, blocking, cand, o, s);
+    case 6: return launch_one<C, 6, 2>(g, w, blocking, cand, o, s);
+    case 7: return launch_one<C, 7, 2>(g, w, blocking, cand, o, s);
+    case 8: return launch_one<C, 8, 2>(g, w, blocking, cand, o, s);
+    case 9: return launch_one<C, 9, 4>(g, w, blocking, cand, o, s);
+    case 10: return launch_one<C, 10, 4>(g, w, blocking, cand, o, s);
+    case 11: return launch_one<C, 11, 4>(g, w, blocking, cand, o, s);
+    default: return launch_one<C, 12, 4>(g, w, blocking, cand, o, s);
   }
 }
 
@@ -365,7 +418,12 @@ hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s) 
   // One launch per blocking (heads grouped by their chosen blocking); a
   // workgroup whose head chose another blocking exits at once.
   for (int c = 0; c < g.nb; ++c) {
-    hipError_t e = (g.d == 128) ? launch_d<128>(g, w, c, cand, o, s) : launch_d<64>(g, w, c, cand, o, s);
+    hipError_t e;
+    if (g.f8)
+      e = (g.d == 128) ? launch_d<F8Core<128>>(g, w, c, cand, o, s) : launch_d<F8Core<64>>(g, w, c, cand, o, s);
+    else
+      e = (g.d == 128) ? launch_d<Bf16Core<128>>(g, w, c, cand, o, s)
+                       : launch_d<Bf16Core<64>>(g, w, c, cand, o, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

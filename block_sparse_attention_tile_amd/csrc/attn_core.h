@@ -59,6 +59,8 @@ struct Lds {
   }
   // V^T row d (channel), 16-byte column c (keys 8c .. 8c+7) -> element offset
   __device__ __forceinline__ static int v_off(int d, int c) { return d * VROW + c * 8; }
+  // key held by physical K row p of a stage
+  __device__ __forceinline__ static int key_of_row(int p) { return (p & ~31) | key_perm(p & 31); }
 };
 
 // A wave's flash-attention state for 32 query rows.

@@ -57,17 +57,112 @@ __device__ __forceinline__ long token_of(const Geo& g, const BlkGeo& b, const Ti
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// ---- E4M3 quantization (VSA_COMPUTE_FP8) ------------------------------------
+// Per (head, tensor) power-of-two factor 2^e: the largest integer e with
+// amax * 2^e <= 448 = 0.875 * 2^9, clamped to [-32, 32] (0 for an all-zero
+// head).  With amax = m * 2^x, m in [0.5, 1): e = 9 - x if m <= 0.875, else
+// 8 - x.  Below 2^-24 the clamp decides (e would exceed 32).
+__device__ __forceinline__ int f8_exponent(uint32_t amax_bf16_bits) {
+  const float a = __uint_as_float(amax_bf16_bits << 16);
+  if (!(a > 0.f)) return 0;
+  if (a < 0x1p-24f) return 32;
+  int x;
+  const float m = frexpf(a, &x);
+  const int e = m <= 0.875f ? 9 - x : 8 - x;
+  return min(max(e, -32), 32);
+}
+
+// Four floats (each |x| <= 448) to E4M3, round to nearest even, packed
+// little-endian (a in the low byte).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// Eight bf16 values (one 16-byte piece) times 2^e to eight E4M3 bytes; the
+// scaling is exact.
+__device__ __forceinline__ uint2 quant8(const uint4& w, int e) {
+  uint2 o;
+  o.x = e4m3x4(ldexpf(bf16_lo(w.x), e), ldexpf(bf16_hi(w.x), e), ldexpf(bf16_lo(w.y), e),
+               ldexpf(bf16_hi(w.y), e));
+  o.y = e4m3x4(ldexpf(bf16_lo(w.z), e), ldexpf(bf16_hi(w.z), e), ldexpf(bf16_lo(w.w), e),
+               ldexpf(bf16_hi(w.w), e));
+  return o;
+}
+
+// Slot (relative to its 32-slot group) stored at position pp of an E4M3 V^T
+// row: slot bits (b4 b3 b2 b1 b0) sit at position (b2 b4 b3 b1 b0), so the
+// keys one MFMA lane half multiplies (bit 2 fixed) are 16 consecutive bytes.
+__device__ __forceinline__ int f8_vslot(int pp) {
+  return (pp & ~31) | (((pp >> 2) & 3) << 3) | (((pp >> 4) & 1) << 2) | (pp & 3);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Partial max |x| (as bf16 bits, sign cleared) of Q, K, V: one workgroup per
+// (slice, head, tensor); slice p covers a contiguous 1/kAmaxParts of the
+// head's N*d raster values.  Integer maxima of the magnitude bits order
+// finite bf16 values exactly; no atomics, so the result is deterministic.
+constexpr int kAmaxThreads = 256;
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(Geo g, const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           uint32_t* __restrict__ part) {
+  const int p = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int which = blockIdx.z;
+  const uint16_t* x = (which == 0 ? q : which == 1 ? k : v) + bh * (long)g.N * g.d;
+  const long n16 = (long)g.N * g.d / 8;  // 16-byte units of the head
+  const long per = (n16 + kAmaxParts - 1) / kAmaxParts;
+  const long lo = p * per;
+  const long hi = min(n16, lo + per);
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+  u16x2 m = {0, 0};
+  constexpr int U = 4;  // loads in flight per thread
+  for (long u0 = lo + threadIdx.x; u0 < hi; u0 += (long)kAmaxThreads * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const long u = u0 + (long)j * kAmaxThreads;
+      w[j] = u < hi ? x4[u] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ww[c] & 0x7fff7fffu));
+    }
+  }
+  uint32_t r = m[0] > m[1] ? m[0] : m[1];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) r = max(r, (uint32_t)__shfl_xor((int)r, o));
+  __shared__ uint32_t wmax[kAmaxThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = wmax[0];
+    for (int i = 1; i < kAmaxThreads / 64; ++i) t = max(t, wmax[i]);
+    part[(bh * 3 + which) * kAmaxParts + p] = t;
+  }
+}
+
 // One workgroup per (head, tile): copies Q and K rows to tile-major order,
 // writes V transposed per tile ([d][slots]) through LDS, and optionally the
 // exact per-tile means of Q and K (fp64 sums of bf16 values, one rounding).
 // The Q/K copy runs first with no barrier in it (four rows per thread in
-// flight); only the V transpose is staged through LDS.
-template <int D>
+// flight); only the V transpose is staged through LDS.  With F8 the copies
+// are E4M3 bytes (per-head power-of-two factors from the partial maxima of
+// amax_kernel, recorded in f8_exp by tile 0) and V^T rows are permuted
+// inside each 32-slot group (f8_vslot); the summaries still use bf16.
+template <int D, bool F8>
 __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ qt, uint16_t* __restrict__ kt,
     uint16_t* __restrict__ vt, float* __restrict__ pooled_q, float* __restrict__ pooled_k,
-    float* __restrict__ pooled_kmin, const int* __restrict__ cand, int pool) {
+    float* __restrict__ pooled_kmin, const int* __restrict__ cand, int pool,
+    const uint32_t* __restrict__ f8_amax, int* __restrict__ f8_exp) {
   constexpr int P = D / 8;                       // 16-byte pieces per row
   constexpr int RPP = kLayoutThreads / P;        // rows per pass
   constexpr int LVW = D / 2 + 1;                 // V chunk row stride in words (odd: no bank conflicts)
@@ -86,6 +181,26 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
   const int r0 = tid / P;
   const long in_base = bh * (long)g.N * D;
   const long tm_base = bh * g.tok_cap * D + (long)i * b.slots * D;
+  uint8_t* const qt8 = reinterpret_cast<uint8_t*>(qt);
+  uint8_t* const kt8 = reinterpret_cast<uint8_t*>(kt);
+  uint8_t* const vt8 = reinterpret_cast<uint8_t*>(vt);
+  int eq = 0, ek = 0, ev = 0;
+  if constexpr (F8) {
+    // every wave reduces the head's partial maxima on its own (no barrier)
+    const int lane = tid & 63;
+    uint32_t m3[3];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      uint32_t m = lane < kAmaxParts ? f8_amax[(bh * 3 + x) * kAmaxParts + lane] : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+      m3[x] = m;
+    }
+    eq = f8_exponent(m3[0]);
+    ek = f8_exponent(m3[1]);
+    ev = f8_exponent(m3[2]);
+    if (i == 0 && tid < 3) f8_exp[bh * 3 + tid] = tid == 0 ? eq : (tid == 1 ? ek : ev);
+  }
 
   double sq[8], sk[8];
   float kmx[8], kmn[8];  // per-channel extrema of K over the valid tokens
@@ -115,8 +230,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * RPP;
       if (s < b.slots) {
-        *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv[u];
-        *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv[u];
+        if constexpr (F8) {
+          *reinterpret_cast<uint2*>(qt8 + tm_base + (long)s * D + p * 8) = quant8(qv[u], eq);
+          *reinterpret_cast<uint2*>(kt8 + tm_base + (long)s * D + p * 8) = quant8(kv[u], ek);
+        } else {
+          *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv[u];
+          *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv[u];
+        }
       }
       if (pool) {
         const uint32_t qw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
@@ -171,8 +291,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
       uint32_t h[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t wv = smem[(s8 * 8 + j) * LVW + (dd >> 1)];
+        const int row = F8 ? f8_vslot(s8 * 8 + j) : s8 * 8 + j;
+        const uint32_t wv = smem[row * LVW + (dd >> 1)];
         h[j] = (dd & 1) ? (wv >> 16) : (wv & 0xffffu);
+      }
+      if constexpr (F8) {
+        uint2 o8;
+        o8.x = e4m3x4(ldexpf(__uint_as_float(h[0] << 16), ev), ldexpf(__uint_as_float(h[1] << 16), ev),
+                      ldexpf(__uint_as_float(h[2] << 16), ev), ldexpf(__uint_as_float(h[3] << 16), ev));
+        o8.y = e4m3x4(ldexpf(__uint_as_float(h[4] << 16), ev), ldexpf(__uint_as_float(h[5] << 16), ev),
+                      ldexpf(__uint_as_float(h[6] << 16), ev), ldexpf(__uint_as_float(h[7] << 16), ev));
+        *reinterpret_cast<uint2*>(vt8 + vt_base + (long)dd * b.slots + sl) = o8;
+        continue;
       }
       uint4 out;
       out.x = h[0] | (h[1] << 16);
@@ -394,18 +524,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
     }
 }
 
+// Explicit instantiations of the layout kernels the launcher picks by value.
+#define VSA_LAYOUT_INST(D, F8)                                                                     \
+  template __global__ void layout_kernel<D, F8>(Geo, const uint16_t*, const uint16_t*,            \
+                                                const uint16_t*, uint16_t*, uint16_t*, uint16_t*, \
+                                                float*, float*, float*, const int*, int,          \
+                                                const uint32_t*, int*);
+VSA_LAYOUT_INST(128, false)
+VSA_LAYOUT_INST(128, true)
+VSA_LAYOUT_INST(64, false)
+VSA_LAYOUT_INST(64, true)
+#undef VSA_LAYOUT_INST
+
 }  // namespace
+
 
 hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, bool pool, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
   const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
-  if (g.d == 128)
-    hipLaunchKernelGGL(layout_kernel<128>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
-                       w.vt, w.pooled_q, w.pooled_k, w.pooled_kmin, cand, pool ? 1 : 0);
-  else
-    hipLaunchKernelGGL(layout_kernel<64>, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt,
-                       w.vt, w.pooled_q, w.pooled_k, w.pooled_kmin, cand, pool ? 1 : 0);
+  auto kern = g.d == 128 ? (g.f8 ? layout_kernel<128, true> : layout_kernel<128, false>)
+                         : (g.f8 ? layout_kernel<64, true> : layout_kernel<64, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt, w.vt,
+                     w.pooled_q, w.pooled_k, w.pooled_kmin, cand, pool ? 1 : 0, w.f8_amax, w.f8_exp);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, hipStream_t s) {
+  hipLaunchKernelGGL(amax_kernel, dim3(kAmaxParts, g.B * g.H, 3), dim3(kAmaxThreads), 0, s, g, q, k,
+                     v, w.f8_amax);
   return hipGetLastError();
 }
 

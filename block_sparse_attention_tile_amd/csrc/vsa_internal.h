@@ -34,6 +34,7 @@ struct Geo {
   double scale;     // softmax scale
   int summ;         // VSA_SUMM_* (dynamic masks)
   int sink;         // leading key tiles kept for every query tile
+  int f8;           // 1 under VSA_COMPUTE_FP8: E4M3 tile-major Q, K, V and attention
   // fine-grained mask
   int fine_M, fine_G;
   long fine_keep;   // kept (group, key) pairs per head (target count)
@@ -87,7 +88,12 @@ struct Ws {
   int* fine_ptr;
   double* fine_score;
   unsigned char* scratch;
+  int* f8_exp;          // [B*H][3] E4M3 scale exponents of Q, K, V
+  uint32_t* f8_amax;    // [B*H][3][kAmaxParts] partial max |x| (bf16 bits)
 };
+
+// Slices per (head, tensor) of the max |x| reduction of the FP8 path.
+constexpr int kAmaxParts = 32;
 
 // Bytes of internal scratch the fine-grained mask needs (fine.hip).
 size_t fine_scratch_bytes(const Geo& g);
@@ -97,6 +103,9 @@ size_t fine_scratch_bytes(const Geo& g);
 // dynamic masks (mean of Q, and mean / max / max+min of K per g.summ).
 hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, bool pool, hipStream_t s);
+// FP8 path: partial max |x| of Q, K, V per head (before launch_layout).
+hipError_t launch_amax(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, hipStream_t s);
 hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s);
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s);

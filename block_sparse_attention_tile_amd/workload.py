@@ -3,7 +3,8 @@ the C structs of the library.
 
 Attributes read: B, H, d, grid, tile, candidates, window, win_mode, topk,
 topk_frac, topp, fine_group, fine_keep, summarizer ("mean", "max" or
-"minmax"; optional, default mean), sink (optional, default 0).
+"minmax"; optional, default mean), sink (optional, default 0), compute
+("bf16" or "fp8"; optional, default bf16).
 """
 from __future__ import annotations
 
@@ -35,5 +36,7 @@ def plan_structs(wl):
     pol = _lib.make_policy(flags_of(wl), win=wl.window or (1, 1, 1), win_mode=mode,
                            topk=wl.topk, topk_frac=wl.topk_frac, topp=wl.topp,
                            fine_group=wl.fine_group, fine_keep=wl.fine_keep,
-                           summarizer=summ, sink=getattr(wl, "sink", 0))
+                           summarizer=summ, sink=getattr(wl, "sink", 0),
+                           compute={"bf16": _lib.VSA_COMPUTE_BF16,
+                                    "fp8": _lib.VSA_COMPUTE_FP8}[getattr(wl, "compute", "bf16")])
     return prob, pol

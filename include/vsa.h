@@ -87,6 +87,26 @@ extern "C" {
 #define VSA_SUMM_MAX    1
 #define VSA_SUMM_MINMAX 2
 
+/* Arithmetic of the tile attention (Sparse VideoGen verdict page,
+ * pith_extraction.core_discovery / forward_implications and
+ * skeptic_critique.rationale: optional FP8 quantization of attention, about
+ * 1.3x on HunyuanVideo, scheme not given).  Readings taken:
+ *   VSA_COMPUTE_BF16  bf16 Q, K, V and probabilities, fp32 accumulation.
+ *   VSA_COMPUTE_FP8   OCP E4M3 (bias 7, largest finite 448, round to nearest
+ *                     even) for Q, K, V and the probabilities.  Per (batch,
+ *                     head) and tensor, x8 = E4M3(x * 2^e) with e the largest
+ *                     integer such that max|x| * 2^e <= 448 (e = 0 when the
+ *                     head is all zeros), clamped to [-32, 32]; inputs need
+ *                     max|x| <= 448 * 2^32.  Scores are the dequantized
+ *                     products s = scale * (q8 . k8) * 2^-(e_q + e_k); with
+ *                     t = s * log2(e) and r = ceil(max t) over the row's kept
+ *                     keys, p8 = E4M3(2^(t - r + 8)); O = 2^-e_v * sum p8 v8 /
+ *                     sum p8, fp32 accumulation.  The selection (SICS, pooled
+ *                     summaries, Top-K / Top-P) still reads the bf16 inputs.
+ *                     Tile masks only (not with VSA_FINE).                  */
+#define VSA_COMPUTE_BF16 0
+#define VSA_COMPUTE_FP8  1
+
 #define VSA_WIN_TRUNCATE 0  /* window cut at the grid edge */
 #define VSA_WIN_CLAMP    1  /* window shifted inward, keeps its full size */
 
@@ -117,6 +137,7 @@ typedef struct vsa_mask_policy {
                              always-kept attention sink (SPADE review page,
                              ledger free parameters: sink length, no value
                              given); 0 = none.  Not with VSA_FINE. */
+  int32_t compute;        /* VSA_COMPUTE_BF16 (0) or VSA_COMPUTE_FP8 */
 } vsa_mask_policy;
 
 /* Opaque, immutable plan; safe to share between threads. */
@@ -161,7 +182,14 @@ typedef struct vsa_plan_info {
 #define VSA_WS_FINE_SCORE 16  /* fp64 [B*H][G][N] group-key scores */
 #define VSA_WS_SCRATCH    17  /* internal */
 #define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][max_tiles][d] per-channel K minimum (VSA_SUMM_MINMAX) */
-#define VSA_WS_NREGIONS   19
+#define VSA_WS_F8_EXP     19  /* int32 [B*H][3] exponents e_q, e_k, e_v (VSA_COMPUTE_FP8) */
+#define VSA_WS_F8_AMAX    20  /* uint32 [B*H][3][parts] partial max |x| as bf16 bits (VSA_COMPUTE_FP8) */
+#define VSA_WS_NREGIONS   21
+/* Under VSA_COMPUTE_FP8 the QT, KT and VT regions hold E4M3 bytes in the
+ * same layouts with 1-byte elements, except that inside every aligned group
+ * of 32 slots of a VT row the key with slot bits (b4 b3 b2 b1 b0) sits at
+ * position (b2 b4 b3 b1 b0): the keys that one half of the 64 MFMA lanes
+ * multiplies are then contiguous. */
 
 /* ---- plan ---------------------------------------------------------------
  * Validates `prob` and `pol`, computes the tile geometry of every blocking,
@@ -169,9 +197,9 @@ typedef struct vsa_plan_info {
  * no HIP call and needs no GPU.  On success *out owns a plan that the caller
  * releases with vsa_plan_destroy.  Errors: VSA_ERR_INVALID_ARG for null
  * pointers, non-positive sizes, even/zero window extents, fractions outside
- * (0,1], conflicting flags; VSA_ERR_UNSUPPORTED for d not in {64,128},
- * dtype other than bf16, more than 4096 tiles, or a tile larger than the
- * grid. */
+ * (0,1], conflicting flags, an unknown compute mode; VSA_ERR_UNSUPPORTED
+ * for d not in {64,128}, dtype other than bf16, VSA_COMPUTE_FP8 with
+ * VSA_FINE, more than 4096 tiles, or a tile larger than the grid. */
 int vsa_plan(const vsa_problem* prob, const vsa_mask_policy* pol, vsa_plan_t** out);
 void vsa_plan_destroy(vsa_plan_t* plan);
 int vsa_plan_get_info(const vsa_plan_t* plan, vsa_plan_info* info);
@@ -228,7 +256,8 @@ int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void*
                void* o, void* workspace, size_t ws_bytes, void* stream);
 
 /* Inverse layout: copy the workspace's tile-major Q (which = 0) or K
- * (which = 1) back to raster bf16 [B, H, N, d] in `out`, dropping pads. */
+ * (which = 1) back to raster bf16 [B, H, N, d] in `out`, dropping pads.
+ * VSA_ERR_UNSUPPORTED under VSA_COMPUTE_FP8 (the workspace holds E4M3). */
 int vsa_untile(const vsa_plan_t* plan, int which, const void* workspace, size_t ws_bytes,
                void* out, void* stream);
 

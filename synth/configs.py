@@ -28,6 +28,7 @@ class Workload:
     fine_keep: float = 0.0
     summarizer: str = "mean"              # block summary of K: "mean", "max", "minmax"
     sink: int = 0                         # leading key tiles always kept
+    compute: str = "bf16"                 # attention arithmetic: "bf16" or "fp8" (E4M3)
     ell: Tuple[float, float, float] = (2.0, 2.0, 2.0)
     ell_alt: Optional[Tuple[float, float, float]] = None  # odd heads
     note: str = ""

@@ -142,8 +142,23 @@ def test_plan_errors():
     assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), sink=-1)) == vsa._lib.VSA_ERR_INVALID_ARG
     assert _err(ok, vsa.make_policy(vsa.VSA_FINE, fine_group=64, fine_keep=0.1, sink=1)) \
         == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), compute=2)) == vsa._lib.VSA_ERR_INVALID_ARG
+    assert _err(ok, vsa.make_policy(vsa.VSA_FINE, fine_group=64, fine_keep=0.1,
+                                    compute=vsa.VSA_COMPUTE_FP8)) == vsa._lib.VSA_ERR_UNSUPPORTED
     with pytest.raises(vsa.VsaError):
         vsa.vsa_plan(None, win) if False else _lib._check(vsa.lib().vsa_plan(None, None, None))
+
+
+def test_fp8_workspace_regions():
+    # E4M3 exponents [B*H][3] and partial maxima [B*H][3][32]; the bf16 plan has neither
+    prob = vsa.make_problem(2, 3, 128, (4, 8, 8), (2, 4, 4))
+    for compute, want_exp, want_amax in ((vsa.VSA_COMPUTE_BF16, 0, 0),
+                                         (vsa.VSA_COMPUTE_FP8, 6 * 3 * 4, 6 * 3 * 32 * 4)):
+        h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), compute=compute))
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_EXP)[1] == want_exp
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_AMAX)[1] == want_amax
+        # tile-major regions keep their bf16 size (E4M3 uses the first half)
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_QT)[1] == 6 * 8 * 32 * 128 * 2
 
 
 def test_exec_argument_errors_before_any_device_call():
