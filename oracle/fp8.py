@@ -41,12 +41,6 @@ def e4m3_decode(codes):
     return sign * mag
 
 
-# every finite non-negative value and its code, ascending
-_POS_CODES = np.array([c for c in range(128) if c != 0x7F], dtype=np.int64)
-_POS_VALUES = e4m3_decode(_POS_CODES)
-_CODE_OF = {float(v): int(c) for v, c in zip(_POS_VALUES, _POS_CODES)}
-
-
 def e4m3_round(x):
     """Round fp64 values to the nearest E4M3 value, ties to even mantissa.
 
@@ -64,10 +58,18 @@ def e4m3_round(x):
 
 
 def e4m3_encode(x):
-    """E4M3 codes of fp64 values (|x| <= 448), round to nearest even."""
+    """E4M3 codes of fp64 values (|x| <= 448), round to nearest even: the
+    bit fields of the rounded value (exponent field E + 7 and mantissa
+    8 * (a / 2^E - 1) for a >= 2^-6; exponent field 0 and mantissa a / 2^-9
+    below)."""
     r = e4m3_round(x)
     a = np.abs(r)
-    codes = np.array([_CODE_OF[float(v)] for v in a.ravel()], dtype=np.int64).reshape(a.shape)
+    _, ex = np.frexp(a)
+    E = ex - 1
+    normal = a >= 2.0 ** -6
+    exp_field = np.where(normal, E + 7, 0)
+    man = np.where(normal, (np.ldexp(a, -E) - 1.0) * 8.0, np.ldexp(a, 9))
+    codes = (exp_field.astype(np.int64) << 3) | man.astype(np.int64)
     # the sign survives rounding to zero (-0 is 0x80), as in IEEE rounding
     return (codes | np.where(np.signbit(r), 0x80, 0)).astype(np.uint8)
 
