@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--sink", type=int, default=None, help="override the workload's sink tiles")
     ap.add_argument("--compute", choices=["bf16", "fp8"], default=None,
                     help="override the attention arithmetic (fp8 = E4M3 Q, K, V and probabilities)")
+    ap.add_argument("--no-fp8-leg", action="store_true",
+                    help="skip the E4M3 (VSA_COMPUTE_FP8) measurement of the same workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -200,6 +202,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                 "traffic": traffic}
 
+    fp8_leg = None
+    if not f8 and not wl.fine_group and not args.no_fp8_leg:
+        fp8_leg = _fp8_leg(wl, q, k, v, o, n_st, stage, flops)
+
     cpu = None
     if args.cpu_budget > 0 and not wl.fine_group and not wl.candidates and not f8:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -233,9 +239,30 @@ def main():
         "attend_tflops": round(attn_tflops, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
+        "fp8": fp8_leg,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def _fp8_leg(wl, q, k, v, o, n, stage, flops):
+    """The same workload and mask with E4M3 attention (VSA_COMPUTE_FP8):
+    whole-call and per-stage times, and the attention kernel against the
+    fp8 MFMA peak."""
+    import block_sparse_attention_tile_amd as vsa
+    from block_sparse_attention_tile_amd.workload import plan_structs
+    print("[bench] E4M3 leg", file=sys.stderr, flush=True)
+    plan8 = vsa.Plan(*plan_structs(wl.with_(compute="fp8")))
+    ms_call = stage(lambda: plan8.forward(q, k, v, o), n)
+    ms_layout = stage(lambda: plan8.layout(q, k, v), n)
+    ms_attend = stage(lambda: plan8.attend(o, q, k, v), n)
+    tf = flops / (ms_attend * 1e-3) / 1e12
+    return {"dtype": "fp8-e4m3", "ms_per_call": round(ms_call, 4),
+            "value": round(flops / (ms_call * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "stages_ms": {"layout": round(ms_layout, 4), "attend": round(ms_attend, 4)},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": _traffic("attend_fp8", wl.name)}}
 
 
 def _mask_desc(wl):
