@@ -20,5 +20,6 @@ Modules:
   fine      - M x 1 fine-grained group mask
   attention - masked softmax attention (dense definition + block-sparse)
   fp8       - E4M3 quantization and the FP8 attention path
+  profile   - online profiling selector (sampled-row MSE against full attention)
 """
-from . import geometry, layout, select, sics, fine, attention, fp8  # noqa: F401
+from . import geometry, layout, select, sics, fine, attention, fp8, profile  # noqa: F401
