@@ -10,7 +10,7 @@ from . import _lib
 from ._lib import (  # noqa: F401
     VSA_DENSE, VSA_FINE, VSA_SICS_SELECT, VSA_TOPK, VSA_TOPK_FRAC, VSA_TOPP, VSA_WINDOW,
     VSA_SUMM_MAX, VSA_SUMM_MEAN, VSA_SUMM_MINMAX, VSA_WIN_CLAMP, VSA_WIN_TRUNCATE, VsaError, lib,
-    VSA_COMPUTE_BF16, VSA_COMPUTE_FP8,
+    VSA_COMPUTE_BF16, VSA_COMPUTE_FP8, VSA_PROFILE_SELECT,
     make_policy, make_problem, vsa_attend,
     vsa_forward, vsa_forward_cached, vsa_layout, vsa_plan, vsa_plan_destroy, vsa_plan_get_info,
     vsa_read_selection, vsa_retained_work, vsa_select, vsa_untile, vsa_workspace_bytes,

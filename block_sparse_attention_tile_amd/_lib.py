@@ -26,6 +26,7 @@ VSA_TOPK_FRAC = 0x08
 VSA_TOPP = 0x10
 VSA_SICS_SELECT = 0x20
 VSA_FINE = 0x40
+VSA_PROFILE_SELECT = 0x80
 VSA_WIN_TRUNCATE = 0
 VSA_WIN_CLAMP = 1
 VSA_MAX_CAND = 4
@@ -39,7 +40,7 @@ VSA_COMPUTE_FP8 = 1
  VSA_WS_COL_IDX, VSA_WS_CAND, VSA_WS_CAND_SCORE, VSA_WS_TILE_SICS, VSA_WS_ATOMS,
  VSA_WS_FINE_QBAR, VSA_WS_FINE_TAU, VSA_WS_FINE_COUNT, VSA_WS_FINE_IDX, VSA_WS_FINE_PTR,
  VSA_WS_FINE_SCORE, VSA_WS_SCRATCH, VSA_WS_POOLED_KMIN, VSA_WS_F8_EXP, VSA_WS_F8_AMAX,
- VSA_WS_NREGIONS) = range(22)
+ VSA_WS_PROF_SSE, VSA_WS_PROF_OFULL, VSA_WS_NREGIONS) = range(24)
 
 EXPORTED = [
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_workspace_bytes",
@@ -60,7 +61,8 @@ class vsa_mask_policy(C.Structure):
     _fields_ = [("flags", C.c_uint32), ("win", C.c_int32 * 3), ("win_mode", C.c_int32),
                 ("topk", C.c_int32), ("topk_frac", C.c_double), ("topp", C.c_double),
                 ("fine_group", C.c_int32), ("fine_keep", C.c_double), ("scale", C.c_double),
-                ("summarizer", C.c_int32), ("sink", C.c_int32), ("compute", C.c_int32)]
+                ("summarizer", C.c_int32), ("sink", C.c_int32), ("compute", C.c_int32),
+                ("profile_frac", C.c_double)]
 
 
 class vsa_plan_info(C.Structure):
@@ -145,7 +147,7 @@ def make_problem(B, H, d, grid, tile, candidates=()):
 
 def make_policy(flags, win=(1, 1, 1), win_mode=VSA_WIN_TRUNCATE, topk=0, topk_frac=0.0,
                 topp=0.0, fine_group=0, fine_keep=0.0, scale=0.0, summarizer=VSA_SUMM_MEAN, sink=0,
-                compute=VSA_COMPUTE_BF16):
+                compute=VSA_COMPUTE_BF16, profile_frac=0.0):
     p = vsa_mask_policy()
     p.flags = flags
     p.win[:] = list(win)
@@ -159,6 +161,7 @@ def make_policy(flags, win=(1, 1, 1), win_mode=VSA_WIN_TRUNCATE, topk=0, topk_fr
     p.summarizer = summarizer
     p.sink = sink
     p.compute = compute
+    p.profile_frac = profile_frac
     return p
 
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("VSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "layout_select.hip", "attend.hip", "sics.hip", "fine.hip"]
+SOURCES = ["api.cpp", "layout_select.hip", "attend.hip", "sics.hip", "fine.hip", "profile.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

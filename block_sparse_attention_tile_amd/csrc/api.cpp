@@ -116,6 +116,8 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.scratch = (unsigned char*)at(VSA_WS_SCRATCH);
   w.f8_exp = (int*)at(VSA_WS_F8_EXP);
   w.f8_amax = (uint32_t*)at(VSA_WS_F8_AMAX);
+  w.prof_sse = (float*)at(VSA_WS_PROF_SSE);
+  w.prof_ofull = (float*)at(VSA_WS_PROF_OFULL);
   return w;
 }
 
@@ -151,7 +153,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   if (N > (1L << 30)) return fail(VSA_ERR_UNSUPPORTED, "too many tokens");
   uint32_t f = po->flags;
   const uint32_t known = VSA_DENSE | VSA_WINDOW | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP |
-                         VSA_SICS_SELECT | VSA_FINE;
+                         VSA_SICS_SELECT | VSA_FINE | VSA_PROFILE_SELECT;
   if (f & ~known) return fail(VSA_ERR_INVALID_ARG, "unknown policy flags 0x%x", f & ~known);
   if (f == 0) return fail(VSA_ERR_INVALID_ARG, "policy selects nothing (flags = 0)");
   if ((f & VSA_FINE) && (f != VSA_FINE))
@@ -160,6 +162,14 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     return fail(VSA_ERR_INVALID_ARG, "VSA_TOPK and VSA_TOPK_FRAC are exclusive");
   if ((f & VSA_SICS_SELECT) && !(f & (VSA_DENSE | VSA_WINDOW | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
     return fail(VSA_ERR_INVALID_ARG, "VSA_SICS_SELECT needs a tile mask to go with it");
+  if ((f & VSA_SICS_SELECT) && (f & VSA_PROFILE_SELECT))
+    return fail(VSA_ERR_INVALID_ARG, "VSA_SICS_SELECT and VSA_PROFILE_SELECT are exclusive");
+  if ((f & VSA_PROFILE_SELECT) && !(f & (VSA_DENSE | VSA_WINDOW)))
+    return fail(VSA_ERR_INVALID_ARG, "VSA_PROFILE_SELECT needs a static tile mask (VSA_DENSE or VSA_WINDOW)");
+  if ((f & VSA_PROFILE_SELECT) && (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
+    return fail(VSA_ERR_UNSUPPORTED, "VSA_PROFILE_SELECT is built for static masks only (no Top-K / Top-P)");
+  if (!(po->profile_frac >= 0.0 && po->profile_frac <= 1.0))
+    return fail(VSA_ERR_INVALID_ARG, "profile_frac must be in (0, 1] (0 selects 0.01)");
   if (!(f & VSA_FINE) && !(f & (VSA_DENSE | VSA_WINDOW | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
     return fail(VSA_ERR_INVALID_ARG, "policy keeps no tiles");
   if (po->scale < 0 || !std::isfinite(po->scale))
@@ -203,7 +213,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     p->dynamic = true;
     p->static_pairs = -1;
   } else {
-    if (f & VSA_SICS_SELECT) {
+    if (f & (VSA_SICS_SELECT | VSA_PROFILE_SELECT)) {
       if (pr->n_cand < 1 || pr->n_cand > VSA_MAX_CAND)
         return fail(VSA_ERR_INVALID_ARG, "n_cand must be in [1, %d]", VSA_MAX_CAND);
       g.nb = pr->n_cand;
@@ -211,7 +221,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       g.nb = 1;
     }
     for (int c = 0; c < g.nb; ++c) {
-      const int32_t* t = (f & VSA_SICS_SELECT) ? pr->cand_tile[c] : pr->tile;
+      const int32_t* t = (f & (VSA_SICS_SELECT | VSA_PROFILE_SELECT)) ? pr->cand_tile[c] : pr->tile;
       BlkGeo& b = g.blk[c];
       long bs = 1;
       for (int a = 0; a < 3; ++a) {
@@ -254,8 +264,8 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
         win_cells *= po->win[a];
       }
     }
-    p->dynamic = (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP | VSA_SICS_SELECT)) != 0;
-    if ((f & (VSA_DENSE | VSA_TOPP)) || (f & VSA_SICS_SELECT)) {
+    p->dynamic = (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP | VSA_SICS_SELECT | VSA_PROFILE_SELECT)) != 0;
+    if ((f & (VSA_DENSE | VSA_TOPP)) || (f & (VSA_SICS_SELECT | VSA_PROFILE_SELECT))) {
       g.row_cap = g.max_tiles;
     } else {
       long cap = win_cells + g.sink;
@@ -263,6 +273,16 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       for (int c = 0; c < g.nb; ++c) maxk = std::max(maxk, g.blk[c].topk);
       cap += maxk;
       g.row_cap = (int)std::min<long>(cap, g.max_tiles);
+    }
+    // Profiling sample: runs of 32 consecutive query rows per head.
+    if (f & VSA_PROFILE_SELECT) {
+      const double frac = po->profile_frac > 0.0 ? po->profile_frac : 0.01;
+      if (N < 32) {
+        g.prof_runs = 1;
+      } else {
+        long r = (long)std::floor(frac * (double)N / 32.0 + 0.5);
+        g.prof_runs = (int)std::min(std::max(r, 1L), N / 32);
+      }
     }
     // SICS atoms: per-axis gcd of the candidate tile extents.
     if (f & VSA_SICS_SELECT) {
@@ -331,6 +351,11 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       sz[VSA_WS_F8_EXP] = (size_t)BH * 3 * 4;
       sz[VSA_WS_F8_AMAX] = (size_t)BH * 3 * vsa::kAmaxParts * 4;
     }
+    if (f & VSA_PROFILE_SELECT) {
+      sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;
+      sz[VSA_WS_PROF_SSE] = (size_t)BH * g.prof_runs * g.nb * 4;
+      sz[VSA_WS_PROF_OFULL] = (size_t)BH * g.prof_runs * 32 * g.d * 4;
+    }
     if (f & VSA_SICS_SELECT) {
       sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;
       sz[VSA_WS_TILE_SICS] = (size_t)BH * g.nb * 2 * g.max_tiles * 4;
@@ -367,6 +392,10 @@ int enqueue_layout(const vsa_plan_t* p, const void* q, const void* k, const void
   if (mask && (g.flags & VSA_SICS_SELECT)) {
     e = vsa::launch_sics(g, w, (const uint16_t*)q, (const uint16_t*)k, s);
     if (e != hipSuccess) return hip_fail(e, "SICS kernels");
+  }
+  if (mask && (g.flags & VSA_PROFILE_SELECT)) {
+    e = vsa::launch_profile(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, s);
+    if (e != hipSuccess) return hip_fail(e, "profiling selector kernels");
   }
   bool pool = mask && (g.flags & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) != 0;
   if (g.f8) {  // the E4M3 scales need every head's max |x| before the layout
@@ -569,7 +598,7 @@ int vsa_read_selection(const vsa_plan_t* p, const void* ws, size_t ws_bytes, int
   hipError_t e = hipMemcpyAsync(len.data(), w.row_len, rows * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(idx.data(), w.col_idx, idx.size() * 4, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess && w.cand && (g.flags & VSA_SICS_SELECT))
+  if (e == hipSuccess && w.cand && vsa::per_head_blocking(g))
     e = hipMemcpyAsync(cnd.data(), w.cand, BH * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "reading the selection");
@@ -626,7 +655,7 @@ int vsa_retained_work(const vsa_plan_t* p, const void* ws, size_t ws_bytes, int6
   hipError_t e = hipMemcpyAsync(len.data(), w.row_len, rows * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(idx.data(), w.col_idx, idx.size() * 4, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess && (g.flags & VSA_SICS_SELECT))
+  if (e == hipSuccess && vsa::per_head_blocking(g))
     e = hipMemcpyAsync(cnd.data(), w.cand, BH * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "reading the selection");

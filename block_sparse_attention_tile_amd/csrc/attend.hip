@@ -414,7 +414,7 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
 }  // namespace
 
 hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s) {
-  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  const int* cand = per_head_blocking(g) ? w.cand : nullptr;
   // One launch per blocking (heads grouped by their chosen blocking); a
   // workgroup whose head chose another blocking exits at once.
   for (int c = 0; c < g.nb; ++c) {

@@ -542,7 +542,7 @@ VSA_LAYOUT_INST(64, true)
 hipError_t launch_layout(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, bool pool, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
-  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  const int* cand = per_head_blocking(g) ? w.cand : nullptr;
   auto kern = g.d == 128 ? (g.f8 ? layout_kernel<128, true> : layout_kernel<128, false>)
                          : (g.f8 ? layout_kernel<64, true> : layout_kernel<64, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kLayoutThreads), 0, s, g, q, k, v, w.qt, w.kt, w.vt,
@@ -559,7 +559,7 @@ hipError_t launch_amax(const Geo& g, const Ws& w, const uint16_t* q, const uint1
 
 hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
-  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  const int* cand = per_head_blocking(g) ? w.cand : nullptr;
   const uint16_t* src = which ? w.kt : w.qt;
   if (g.d == 128)
     hipLaunchKernelGGL(untile_kernel<128>, grid, dim3(kLayoutThreads), 0, s, g, src, cand, out);
@@ -570,7 +570,7 @@ hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hi
 
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
-  const int* cand = (g.flags & VSA_SICS_SELECT) ? w.cand : nullptr;
+  const int* cand = per_head_blocking(g) ? w.cand : nullptr;
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, g, w.pooled_q, w.pooled_k, w.pooled_kmin, cand,
                      w.row_len, w.col_idx);
   return hipGetLastError();

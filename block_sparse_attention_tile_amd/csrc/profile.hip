@@ -1,0 +1,419 @@
+// Online profiling selector (VSA_PROFILE_SELECT): per head, the candidate
+// blocking whose masked attention on a sample of query rows is closest, in
+// mean squared error, to full attention on the same rows (Sparse VideoGen
+// verdict page, pith_extraction.key_machinery and core_discovery: spatial vs
+// temporal heads decided by a ~1% row sample).
+//
+// Readings: the candidates are the plan's candidate blockings under the
+// policy's static tile mask (window and / or sink, or dense); the sample is
+// an evenly spread set of runs of 32 consecutive raster tokens; MSE is the
+// mean over the sampled rows and channels; ties go to the lower candidate.
+//
+// profile_full_kernel: one wave per (head, run of 32 query rows) sweeps all
+// keys, line by line of the raster grid (a line = the W tokens of one
+// (t, h)), in chunks of up to 64 keys staged in LDS (K by direct loads in
+// MFMA lane order, V transposed through VGPRs), and stores the full
+// attention outputs of the run in fp32.
+// profile_masked_kernel: one wave per (head, run, candidate) visits only the
+// lines that some row's kept keys reach.  A candidate's kept keys on a line
+// are, per query row, one interval of w (its window is a box of token
+// coordinates) plus, for every row alike, one interval of sink tiles; the
+// wave sums the squared differences of its masked outputs to the full ones.
+//
+// choose_profile_kernel: per head, the MSE of every candidate (fixed-order
+// sums over the runs) and the argmin, into the workspace's CAND /
+// CAND_SCORE regions that the layout, selection and attention read.
+#include <hip/hip_runtime.h>
+
+#include "attn_core.h"
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+using core::bf16x2;
+using core::bf16x8;
+using core::f32x16;
+using core::kKC;
+using core::Lds;
+
+constexpr int kRun = 32;  // query rows per sampled run (one wave)
+
+// Inclusive token range of axis a kept by a blocking's window around the
+// query coordinate x (the window is in tiles; clamp mode shifts it inward).
+__device__ __forceinline__ void window_axis(const Geo& g, const BlkGeo& b, int a, int x, int* lo,
+                                            int* hi) {
+  const int tile = a == 0 ? b.tile[0] : (a == 1 ? b.tile[1] : b.tile[2]);
+  const int n = a == 0 ? b.nt[0] : (a == 1 ? b.nt[1] : b.nt[2]);
+  const int grid = a == 0 ? g.grid[0] : (a == 1 ? g.grid[1] : g.grid[2]);
+  const int win = a == 0 ? g.win[0] : (a == 1 ? g.win[1] : g.win[2]);
+  if ((g.flags & VSA_DENSE) || !(g.flags & VSA_WINDOW)) {
+    *lo = 0;
+    *hi = grid - 1;
+    return;
+  }
+  const int c = x / tile;
+  const int r = (win - 1) / 2;
+  int tl, th;
+  if (g.win_mode == VSA_WIN_CLAMP && n >= 2 * r + 1) {
+    tl = min(max(c - r, 0), n - (2 * r + 1));
+    th = tl + 2 * r;
+  } else {
+    tl = max(c - r, 0);
+    th = min(c + r, n - 1);
+  }
+  *lo = tl * tile;
+  *hi = min((th + 1) * tile, grid) - 1;
+}
+
+// Accumulators of one candidate's masked attention.  Unlike the tile path,
+// a row may see no kept key in a block (masks differ per row), so a row
+// whose reference is still -inf takes zero probabilities instead of
+// exp2(-inf + inf).
+template <int D>
+struct MaskedAcc {
+  static constexpr int DT = D / 32;
+  f32x16 acc[DT];
+  float mo;
+  float l_part;
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    mo = -INFINITY;
+    l_part = 0.f;
+  }
+
+  __device__ __forceinline__ void softmax(const f32x16& s, float c2, bf16x8 pb[2]) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float mxc = mx * c2;
+    if (__any(mxc - mo > 8.0f)) {
+      const float mn = fmaxf(mo, ceilf(fmaxf(mxc, __shfl_xor(mxc, 32))));
+      const float alpha = mo == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.0f, (int)(mo - mn));
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      mo = mn;
+    }
+    const float off = mo == -INFINITY ? 0.f : mo;  // no key yet: every s is -inf
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pb[half][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[half * 8 + t], c2, -off));
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        bf16x2 pr = {pb[half][t], pb[half][t + 1]};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, core::kOnes2, l_part, false);
+      }
+  }
+
+  __device__ __forceinline__ void pv(const uint16_t* lvt, int kb, int col, int hi, const bf16x8 pb[2]) {
+    const uint16_t* vp = lvt + col * Lds<D>::VROW + kb * 32 + hi * 8;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], acc[dt], 0, 0, 0);
+      }
+  }
+};
+
+// Keys of a 32-key block outside [a1, b1] and [a2, b2] (block-relative key
+// indices) get -inf.  Register r of lane half hi holds key 16*(r/8) +
+// 8*hi + r%8 of the block (the lane order of attn_core.h); the thresholds
+// are shifted by 8*hi and laundered so the compares stay against
+// immediates.
+__device__ __forceinline__ void mask_intervals(f32x16& s, int a1, int b1, int a2, int b2, int hi) {
+  int t0 = a1 - 8 * hi, t1 = b1 - 8 * hi, t2 = a2 - 8 * hi, t3 = b2 - 8 * hi;
+  asm volatile("" : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = 16 * (r >> 3) + (r & 7);
+    const bool keep = (j >= t0 && j <= t1) || (j >= t2 && j <= t3);
+    if (!keep) s[r] = -INFINITY;
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Stage up to 64 consecutive raster keys (nk valid) into LDS.  K: direct
+// global->LDS loads into the padded, lane-ordered rows of Lds<D> (each
+// instruction fills 1 KB; rows past nk re-read row nk-1, which the masks
+// drop).  V^T: through VGPRs, one channel pair per lane (with d = 64 the two
+// lane halves split the keys), 8 keys per batch, keys past nk zero.
+template <int D>
+__device__ __forceinline__ void stage_keys(uint16_t* lk, uint16_t* lvt, const uint16_t* __restrict__ k0,
+                                           const uint16_t* __restrict__ v0, int nk, int lane) {
+  constexpr int KC16 = Lds<D>::KC16;
+  constexpr int KI = kKC * (KC16 + 1) / 64;  // 1 KB instructions of the K part
+#pragma unroll
+  for (int ins = 0; ins < KI; ++ins) {
+    const int u = ins * 64 + lane;
+    const int p = u / (KC16 + 1);
+    const int c = min(u % (KC16 + 1), KC16 - 1);
+    const int key = min(Lds<D>::key_of_row(p), nk - 1);
+    __builtin_amdgcn_global_load_lds(k0 + (long)key * D + c * 8, (lds_ptr_t)(lk + ins * 512), 16, 0, 0);
+  }
+  constexpr int PAIRS = D / 2;
+  static_assert(PAIRS == 64 || PAIRS == 32, "d is 64 or 128");
+  constexpr int KEYS = PAIRS == 64 ? 64 : 32;  // keys handled by one lane
+  const int pp = lane % PAIRS;
+  const int k_first = (lane / PAIRS) * KEYS;
+#pragma unroll 1
+  for (int g8 = 0; g8 < KEYS / 8; ++g8) {
+    uint32_t wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = k_first + g8 * 8 + j;
+      wv[j] = key < nk ? *reinterpret_cast<const uint32_t*>(v0 + (long)key * D + 2 * pp) : 0u;
+    }
+    uint4 lo, hv;
+    lo.x = (wv[0] & 0xffffu) | (wv[1] << 16);
+    lo.y = (wv[2] & 0xffffu) | (wv[3] << 16);
+    lo.z = (wv[4] & 0xffffu) | (wv[5] << 16);
+    lo.w = (wv[6] & 0xffffu) | (wv[7] << 16);
+    hv.x = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
+    hv.y = (wv[2] >> 16) | (wv[3] & 0xffff0000u);
+    hv.z = (wv[4] >> 16) | (wv[5] & 0xffff0000u);
+    hv.w = (wv[6] >> 16) | (wv[7] & 0xffff0000u);
+    const int c = k_first / 8 + g8;
+    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp, c)) = lo;
+    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp + 1, c)) = hv;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct loads have landed
+}
+
+// Full attention of one run of 32 sampled query rows over all keys (the
+// reference outputs), written to ofull [B*H][runs][32][d] in fp32.
+template <int D>
+__global__ __launch_bounds__(64, 1) void profile_full_kernel(Geo g, const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v,
+                                                            float* __restrict__ ofull) {
+  __shared__ __align__(16) uint16_t lds[Lds<D>::STAGE];
+  uint16_t* const lk = lds;
+  uint16_t* const lvt = lds + Lds<D>::KE;
+  const int run = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int col = lane & 31, hi = lane >> 5;
+  const long N = g.N;
+  const long row0 = N < kRun ? 0 : (long)run * N / g.prof_runs;
+  const long qtok = min(row0 + col, N - 1);
+  const long head = bh * N * D;
+  const int W = g.grid[2];
+  const long lines = (long)g.grid[0] * g.grid[1];
+
+  core::WaveState<D> full;
+  full.init(q + head + qtok * D, hi);
+  const float c2 = (float)(g.scale * 1.4426950408889634);
+  for (long line = 0; line < lines; ++line) {
+    for (int w0 = 0; w0 < W; w0 += kKC) {
+      const int nk = min(kKC, W - w0);
+      __syncthreads();  // the previous chunk's reads are done
+      const long key0 = line * W + w0;
+      stage_keys<D>(lk, lvt, k + head + key0 * D, v + head + key0 * D, nk, lane);
+      __syncthreads();
+      for (int kb = 0; kb < 2; ++kb) {
+        const int nkb = nk - 32 * kb;
+        if (nkb <= 0) break;
+        f32x16 s = full.scores(lk, kb, col, hi);
+        if (nkb < 32) core::WaveState<D>::mask(s, nkb, hi);
+        bf16x8 pb[2];
+        full.softmax(s, c2, pb);
+        full.pv(lvt, kb, col, hi, pb);
+      }
+    }
+  }
+  const float l = full.l_part + __shfl_xor(full.l_part, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* out = ofull + ((bh * g.prof_runs + run) * kRun + col) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 x;
+      x.x = full.acc[dt][4 * r4 + 0] * inv;
+      x.y = full.acc[dt][4 * r4 + 1] * inv;
+      x.z = full.acc[dt][4 * r4 + 2] * inv;
+      x.w = full.acc[dt][4 * r4 + 3] * inv;
+      *reinterpret_cast<float4*>(out + dt * 32 + 8 * r4 + 4 * hi) = x;
+    }
+}
+
+// One candidate (blockIdx.z) on one run: the masked attention of the 32
+// rows over the keys its static mask keeps, and the sum over the rows and
+// channels of the squared difference to the full outputs.  Only lines that
+// some row's window box or the sink reaches are visited, and on each only
+// the hull of those w ranges.
+template <int D>
+__global__ __launch_bounds__(64, 1) void profile_masked_kernel(Geo g, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              const float* __restrict__ ofull,
+                                                              float* __restrict__ sse) {
+  __shared__ __align__(16) uint16_t lds[Lds<D>::STAGE];
+  uint16_t* const lk = lds;
+  uint16_t* const lvt = lds + Lds<D>::KE;
+  const int run = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int cand = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int col = lane & 31, hi = lane >> 5;
+  const int T = g.grid[0], H = g.grid[1], W = g.grid[2];
+  const long N = g.N;
+  const long row0 = N < kRun ? 0 : (long)run * N / g.prof_runs;
+  const bool valid = row0 + col < N;
+  const long qtok = min(row0 + col, N - 1);
+  const long head = bh * N * D;
+  const BlkGeo b = pick_blk(g, cand);
+
+  core::WaveState<D> qs;  // Q fragments and the score product only
+  qs.init(q + head + qtok * D, hi);
+  MaskedAcc<D> acc;
+  acc.reset();
+  const int qt = (int)(qtok / ((long)H * W)), qh = (int)((qtok / W) % H), qw = (int)(qtok % W);
+  int blo[3], bhi[3];
+  window_axis(g, b, 0, qt, &blo[0], &bhi[0]);
+  window_axis(g, b, 1, qh, &blo[1], &bhi[1]);
+  window_axis(g, b, 2, qw, &blo[2], &bhi[2]);
+  // wave-uniform hull of the rows' boxes
+  int ulo[3], uhi[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    int lo = blo[a], hv = bhi[a];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      lo = min(lo, __shfl_xor(lo, m));
+      hv = max(hv, __shfl_xor(hv, m));
+    }
+    ulo[a] = __builtin_amdgcn_readfirstlane(lo);
+    uhi[a] = __builtin_amdgcn_readfirstlane(hv);
+  }
+  const float c2 = (float)(g.scale * 1.4426950408889634);
+
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      const bool box_line = t >= ulo[0] && t <= uhi[0] && h >= ulo[1] && h <= uhi[1];
+      // sink tiles on this line: tile index base + w / tw < sink
+      const int base = ((t / b.tile[0]) * b.nt[1] + h / b.tile[1]) * b.nt[2];
+      const int ms = g.sink - base;
+      const int sink_end = ms > 0 ? (int)min((long)ms * b.tile[2], (long)W) : 0;  // w < sink_end
+      if (!box_line && sink_end == 0) continue;
+      int w_lo = box_line ? ulo[2] : W, w_hi = box_line ? uhi[2] : -1;
+      if (sink_end > 0) {
+        w_lo = 0;
+        w_hi = max(w_hi, sink_end - 1);
+      }
+      // this row's interval on the line (box) and the line's sink interval
+      const bool in = t >= blo[0] && t <= bhi[0] && h >= blo[1] && h <= bhi[1];
+      const int ba = in ? blo[2] : 1, bb = in ? bhi[2] : 0;
+      const long line = ((long)t * H + h) * W;
+      for (int w0 = w_lo; w0 <= w_hi; w0 += kKC) {
+        const int nk = min(kKC, w_hi + 1 - w0);
+        __syncthreads();
+        stage_keys<D>(lk, lvt, k + head + (line + w0) * D, v + head + (line + w0) * D, nk, lane);
+        __syncthreads();
+        for (int kb = 0; kb < 2; ++kb) {
+          const int nkb = nk - 32 * kb;
+          if (nkb <= 0) break;
+          const int lo_k = w0 + 32 * kb, hi_k = lo_k + min(nkb, 32) - 1;  // w of the block's keys
+          const int a1 = max(ba, lo_k), b1 = min(bb, hi_k);
+          const int a2 = lo_k, b2 = min(sink_end - 1, hi_k);
+          if (!__any(a1 <= b1 || a2 <= b2)) continue;  // no row keeps a key of this block
+          f32x16 s = qs.scores(lk, kb, col, hi);
+          mask_intervals(s, a1 - lo_k, b1 - lo_k, a2 - lo_k, b2 - lo_k, hi);
+          bf16x8 pb[2];
+          acc.softmax(s, c2, pb);
+          acc.pv(lvt, kb, col, hi, pb);
+        }
+      }
+    }
+  }
+
+  const float l = acc.l_part + __shfl_xor(acc.l_part, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float* ref = ofull + ((bh * g.prof_runs + run) * kRun + col) * D;
+  float e = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 x = *reinterpret_cast<const float4*>(ref + dt * 32 + 8 * r4 + 4 * hi);
+      const float d0 = acc.acc[dt][4 * r4 + 0] * inv - x.x, d1 = acc.acc[dt][4 * r4 + 1] * inv - x.y;
+      const float d2 = acc.acc[dt][4 * r4 + 2] * inv - x.z, d3 = acc.acc[dt][4 * r4 + 3] * inv - x.w;
+      e = fmaf(d0, d0, e);
+      e = fmaf(d1, d1, e);
+      e = fmaf(d2, d2, e);
+      e = fmaf(d3, d3, e);
+    }
+  if (!valid) e = 0.f;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) e += __shfl_xor(e, m);
+  if (lane == 0) sse[(bh * g.prof_runs + run) * g.nb + cand] = e;
+}
+
+// Per head: MSE of every candidate (runs summed in order, fp64) and the
+// argmin (ties to the lower index).
+__global__ void choose_profile_kernel(Geo g, const float* __restrict__ sse, float* __restrict__ score,
+                                      int* __restrict__ cand) {
+  const long bh = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= (long)g.B * g.H) return;
+  const double rows = (double)(g.N < kRun ? g.N : (long)kRun * g.prof_runs);
+  int best = 0;
+  double best_v = 0.0;
+  for (int c = 0; c < g.nb; ++c) {
+    double s = 0.0;
+    for (int r = 0; r < g.prof_runs; ++r) s += (double)sse[(bh * g.prof_runs + r) * g.nb + c];
+    const double mse = s / (rows * g.d);
+    score[bh * g.nb + c] = (float)mse;
+    if (c == 0 || mse < best_v) {
+      best = c;
+      best_v = mse;
+    }
+  }
+  cand[bh] = best;
+}
+
+// Explicit instantiations of the kernels the launcher picks.
+template __global__ void profile_full_kernel<128>(Geo, const uint16_t*, const uint16_t*, const uint16_t*, float*);
+template __global__ void profile_full_kernel<64>(Geo, const uint16_t*, const uint16_t*, const uint16_t*, float*);
+template __global__ void profile_masked_kernel<128>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
+                                                    const float*, float*);
+template __global__ void profile_masked_kernel<64>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
+                                                   const float*, float*);
+
+template <int D>
+hipError_t launch_profile_d(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, hipStream_t s) {
+  hipLaunchKernelGGL(profile_full_kernel<D>, dim3(g.prof_runs, g.B * g.H), dim3(64), 0, s, g, q, k, v,
+                     w.prof_ofull);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(profile_masked_kernel<D>, dim3(g.prof_runs, g.B * g.H, g.nb), dim3(64), 0, s, g, q,
+                     k, v, w.prof_ofull, w.prof_sse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_profile(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, hipStream_t s) {
+  hipError_t e = g.d == 128 ? launch_profile_d<128>(g, w, q, k, v, s) : launch_profile_d<64>(g, w, q, k, v, s);
+  if (e != hipSuccess) return e;
+  const int BH = g.B * g.H;
+  hipLaunchKernelGGL(choose_profile_kernel, dim3((BH + 255) / 256), dim3(256), 0, s, g, w.prof_sse,
+                     w.cand_score, w.cand);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -35,6 +35,7 @@ struct Geo {
   int summ;         // VSA_SUMM_* (dynamic masks)
   int sink;         // leading key tiles kept for every query tile
   int f8;           // 1 under VSA_COMPUTE_FP8: E4M3 tile-major Q, K, V and attention
+  int prof_runs;    // VSA_PROFILE_SELECT: sampled runs of 32 query rows per head
   // fine-grained mask
   int fine_M, fine_G;
   long fine_keep;   // kept (group, key) pairs per head (target count)
@@ -50,7 +51,13 @@ struct Geo {
 __host__ __device__ __forceinline__ int sel4(int c, int a0, int a1, int a2, int a3) {
   return c == 0 ? a0 : (c == 1 ? a1 : (c == 2 ? a2 : a3));
 }
-// The blocking chosen for head bh (0 without SICS selection), clamped to a
+// Whether the blocking is chosen per head (by SICS or by the profiling
+// selector; both write the workspace's CAND region).
+__host__ __device__ __forceinline__ bool per_head_blocking(const Geo& g) {
+  return (g.flags & (VSA_SICS_SELECT | VSA_PROFILE_SELECT)) != 0;
+}
+
+// The blocking chosen for head bh (0 without a per-head choice), clamped to a
 // valid index, so that a workspace whose selection was never written (a
 // cached call on a fresh workspace) still addresses memory in bounds.
 __device__ __forceinline__ int cand_of(const Geo& g, const int* cand, long bh) {
@@ -90,6 +97,8 @@ struct Ws {
   unsigned char* scratch;
   int* f8_exp;          // [B*H][3] E4M3 scale exponents of Q, K, V
   uint32_t* f8_amax;    // [B*H][3][kAmaxParts] partial max |x| (bf16 bits)
+  float* prof_sse;      // [B*H][prof_runs][nb] squared-error sums of the profiling selector
+  float* prof_ofull;    // [B*H][prof_runs][32][d] full-attention outputs of the sampled rows
 };
 
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.
@@ -111,6 +120,10 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s);
 hipError_t launch_sics(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                        hipStream_t s);
+// Profiling selector: per-head MSE of every candidate on the sampled rows,
+// and the chosen blocking (CAND, CAND_SCORE).
+hipError_t launch_profile(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, hipStream_t s);
 hipError_t launch_fine_select(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                               hipStream_t s);
 hipError_t launch_fine_attend(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,

@@ -4,7 +4,9 @@ the C structs of the library.
 Attributes read: B, H, d, grid, tile, candidates, window, win_mode, topk,
 topk_frac, topp, fine_group, fine_keep, summarizer ("mean", "max" or
 "minmax"; optional, default mean), sink (optional, default 0), compute
-("bf16" or "fp8"; optional, default bf16).
+("bf16" or "fp8"; optional, default bf16), selector ("sics" or "profile":
+how a head picks among the candidates; optional, default sics) and
+profile_frac (optional, default 0 = 1%).
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ def flags_of(wl):
     if wl.topp:
         f |= _lib.VSA_TOPP
     if wl.candidates:
-        f |= _lib.VSA_SICS_SELECT
+        f |= _lib.VSA_PROFILE_SELECT if getattr(wl, "selector", "sics") == "profile" else _lib.VSA_SICS_SELECT
     return f or _lib.VSA_DENSE
 
 
@@ -38,5 +40,6 @@ def plan_structs(wl):
                            fine_group=wl.fine_group, fine_keep=wl.fine_keep,
                            summarizer=summ, sink=getattr(wl, "sink", 0),
                            compute={"bf16": _lib.VSA_COMPUTE_BF16,
-                                    "fp8": _lib.VSA_COMPUTE_FP8}[getattr(wl, "compute", "bf16")])
+                                    "fp8": _lib.VSA_COMPUTE_FP8}[getattr(wl, "compute", "bf16")],
+                           profile_frac=getattr(wl, "profile_frac", 0.0))
     return prob, pol

@@ -59,6 +59,19 @@ extern "C" {
  * VSA_TOPP        smallest set of highest-scoring key tiles whose softmax
  *                 mass over the row reaches `topp`.
  * VSA_SICS_SELECT per head, pick among problem.cand_tile[] by SICS.
+ * VSA_PROFILE_SELECT per head, pick among problem.cand_tile[] the blocking
+ *                 whose masked attention on a sample of query rows is
+ *                 closest (MSE) to full attention on them (Sparse VideoGen
+ *                 verdict page, pith_extraction.key_machinery: spatial vs
+ *                 temporal heads from a ~1% row sample).  Readings: the
+ *                 candidates use the policy's static mask (VSA_DENSE or
+ *                 VSA_WINDOW, plus the sink); the sample is
+ *                 clamp(round(profile_frac * N / 32), 1, N / 32) runs of 32
+ *                 consecutive raster tokens, run r starting at
+ *                 floor(r * N / runs) (all N tokens when N < 32); MSE is the
+ *                 mean over sampled rows and channels; ties go to the lower
+ *                 candidate.  Exclusive with VSA_SICS_SELECT; dynamic masks
+ *                 (Top-K / Top-P) with it are VSA_ERR_UNSUPPORTED.
  * VSA_FINE        fine-grained M x 1 mask (M = fine_group), keep fraction
  *                 fine_keep of all (group, key) pairs per head.  Exclusive
  *                 with every other flag.
@@ -71,6 +84,7 @@ extern "C" {
 #define VSA_TOPP         0x10u
 #define VSA_SICS_SELECT  0x20u
 #define VSA_FINE         0x40u
+#define VSA_PROFILE_SELECT 0x80u
 
 /* Block summarizer and score estimator of dynamic (Top-K / Top-P) masks.
  * The SPADE review page (referee report, minor comment 3; its ledger of
@@ -116,7 +130,7 @@ typedef struct vsa_problem {
   int32_t B, H, d;
   int32_t grid[3];                    /* T, H, W in tokens */
   int32_t tile[3];                    /* tile extents (t, h, w) when SICS is off */
-  int32_t n_cand;                     /* candidate blockings for SICS (<= 4) */
+  int32_t n_cand;                     /* candidate blockings for SICS / profiling (<= 4) */
   int32_t cand_tile[VSA_MAX_CAND][3];
   int32_t dtype;                      /* VSA_BF16 */
 } vsa_problem;
@@ -138,6 +152,8 @@ typedef struct vsa_mask_policy {
                              ledger free parameters: sink length, no value
                              given); 0 = none.  Not with VSA_FINE. */
   int32_t compute;        /* VSA_COMPUTE_BF16 (0) or VSA_COMPUTE_FP8 */
+  double profile_frac;    /* VSA_PROFILE_SELECT: sampled fraction of query
+                             rows, in (0, 1]; 0 selects 0.01 */
 } vsa_mask_policy;
 
 /* Opaque, immutable plan; safe to share between threads. */
@@ -145,7 +161,7 @@ typedef struct vsa_plan_s vsa_plan_t;
 
 /* Facts about a plan (host data). */
 typedef struct vsa_plan_info {
-  int32_t n_blockings;            /* 1, or n_cand under VSA_SICS_SELECT */
+  int32_t n_blockings;            /* 1, or n_cand under VSA_SICS_SELECT / VSA_PROFILE_SELECT */
   int32_t ntiles[VSA_MAX_CAND][3];/* tiles per axis of each blocking */
   int32_t n_tiles[VSA_MAX_CAND];  /* tiles of each blocking */
   int32_t slots[VSA_MAX_CAND];    /* tokens per tile rounded up to 32 */
@@ -171,7 +187,7 @@ typedef struct vsa_plan_info {
 #define VSA_WS_ROW_LEN     5  /* int32 [B*H][max_tiles] kept tiles per row */
 #define VSA_WS_COL_IDX     6  /* int32 [B*H][max_tiles][row_cap] ascending */
 #define VSA_WS_CAND        7  /* int32 [B*H] chosen blocking */
-#define VSA_WS_CAND_SCORE  8  /* fp32 [B*H][n_blockings] mean pair cosine */
+#define VSA_WS_CAND_SCORE  8  /* fp32 [B*H][n_blockings] mean pair cosine (SICS) or MSE (profiling) */
 #define VSA_WS_TILE_SICS   9  /* fp32 [B*H][n_blockings][2][max_tiles] SICS of Q, K */
 #define VSA_WS_ATOMS      10  /* fp32 [B*H][2][atoms][d] unit-vector sums, then int32 [B*H][2][atoms] non-zero counts */
 #define VSA_WS_FINE_QBAR  11  /* fp32 [B*H][G][d] group means of Q */
@@ -184,7 +200,9 @@ typedef struct vsa_plan_info {
 #define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][max_tiles][d] per-channel K minimum (VSA_SUMM_MINMAX) */
 #define VSA_WS_F8_EXP     19  /* int32 [B*H][3] exponents e_q, e_k, e_v (VSA_COMPUTE_FP8) */
 #define VSA_WS_F8_AMAX    20  /* uint32 [B*H][3][parts] partial max |x| as bf16 bits (VSA_COMPUTE_FP8) */
-#define VSA_WS_NREGIONS   21
+#define VSA_WS_PROF_SSE   21  /* fp32 [B*H][runs][n_blockings] squared-error sums (VSA_PROFILE_SELECT) */
+#define VSA_WS_PROF_OFULL 22  /* fp32 [B*H][runs][32][d] full-attention outputs of the sampled rows */
+#define VSA_WS_NREGIONS   23
 /* Under VSA_COMPUTE_FP8 the QT, KT and VT regions hold E4M3 bytes in the
  * same layouts with 1-byte elements, except that inside every aligned group
  * of 32 slots of a VT row the key with slot bits (b4 b3 b2 b1 b0) sits at
@@ -236,7 +254,8 @@ int vsa_forward_cached(const vsa_plan_t* plan, const void* q, const void* k, con
                        void* o, void* workspace, size_t ws_bytes, void* stream);
 
 /* Stage 1, layout: under VSA_SICS_SELECT scores every candidate blocking by
- * SICS and records the chosen one per head; then copies Q, K (tile-major)
+ * SICS (under VSA_PROFILE_SELECT by the sampled-row MSE) and records the
+ * chosen one per head; then copies Q, K (tile-major)
  * and V (tile-major, transposed per tile) into the workspace, padding each
  * tile with zeros up to its slot count, and, for dynamic masks, writes the
  * per-tile mean of Q and K.  Nothing to do under VSA_FINE. */

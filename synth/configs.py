@@ -29,6 +29,8 @@ class Workload:
     summarizer: str = "mean"              # block summary of K: "mean", "max", "minmax"
     sink: int = 0                         # leading key tiles always kept
     compute: str = "bf16"                 # attention arithmetic: "bf16" or "fp8" (E4M3)
+    selector: str = "sics"                # per-head choice among candidates: "sics" or "profile"
+    profile_frac: float = 0.0             # sampled query rows of the profiling selector (0 = 1%)
     ell: Tuple[float, float, float] = (2.0, 2.0, 2.0)
     ell_alt: Optional[Tuple[float, float, float]] = None  # odd heads
     note: str = ""

@@ -203,3 +203,15 @@ def test_workspace_regions_disjoint_and_aligned():
     spans.sort()
     for a, b in zip(spans, spans[1:]):
         assert a[1] <= b[0]
+
+
+def test_profile_errors_and_sizes():
+    prob = vsa.make_problem(1, 2, 64, (4, 8, 8), (2, 4, 4), candidates=((2, 4, 4), (4, 2, 2)))
+    bad = vsa.make_policy(vsa.VSA_PROFILE_SELECT | vsa.VSA_TOPK, topk=2)
+    with pytest.raises(vsa.VsaError):
+        vsa.vsa_plan(prob, bad)
+    h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_PROFILE_SELECT | vsa.VSA_WINDOW, win=(1, 1, 1),
+                                           profile_frac=0.5))
+    runs = 4  # round(0.5 * 256 / 32)
+    assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_SSE)[1] == 2 * runs * 2 * 4
+    assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_OFULL)[1] == 2 * runs * 32 * 64 * 4
