@@ -276,7 +276,11 @@ def _mask_desc(wl):
     if wl.topp:
         parts.append(f"top-p {wl.topp}")
     if wl.candidates:
-        parts.append("SICS blocking choice per head")
+        if wl.selector == "profile":
+            parts.append(f"profiling selector per head ({(wl.profile_frac or 0.01):.0%} of query rows, "
+                         f"candidates {' / '.join('x'.join(map(str, c)) for c in wl.candidates)})")
+        else:
+            parts.append("SICS blocking choice per head")
     if wl.fine_group:
         parts.append(f"fine M={wl.fine_group} keep {wl.fine_keep:.0%}")
     if (wl.topk or wl.topk_frac or wl.topp) and wl.summarizer != "mean":

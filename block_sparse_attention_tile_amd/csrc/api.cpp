@@ -117,7 +117,7 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.f8_exp = (int*)at(VSA_WS_F8_EXP);
   w.f8_amax = (uint32_t*)at(VSA_WS_F8_AMAX);
   w.prof_sse = (float*)at(VSA_WS_PROF_SSE);
-  w.prof_ofull = (float*)at(VSA_WS_PROF_OFULL);
+  w.prof_part = (float*)at(VSA_WS_PROF_PART);
   return w;
 }
 
@@ -283,6 +283,11 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
         long r = (long)std::floor(frac * (double)N / 32.0 + 0.5);
         g.prof_runs = (int)std::min(std::max(r, 1L), N / 32);
       }
+      // split the keys into ranges of lines until the full pass has about
+      // 1024 workgroups of four runs (two rounds of two per CU)
+      const long groups = (long)g.B * g.H * ((g.prof_runs + 3) / 4);
+      const long lines = (long)pr->grid[0] * pr->grid[1];
+      g.prof_segs = (int)std::max(1L, std::min({(1024 + groups - 1) / groups, lines, 16L}));
     }
     // SICS atoms: per-axis gcd of the candidate tile extents.
     if (f & VSA_SICS_SELECT) {
@@ -354,7 +359,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     if (f & VSA_PROFILE_SELECT) {
       sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;
       sz[VSA_WS_PROF_SSE] = (size_t)BH * g.prof_runs * g.nb * 4;
-      sz[VSA_WS_PROF_OFULL] = (size_t)BH * g.prof_runs * 32 * g.d * 4;
+      sz[VSA_WS_PROF_PART] = (size_t)BH * g.prof_runs * g.prof_segs * 32 * (g.d + 2) * 4;
     }
     if (f & VSA_SICS_SELECT) {
       sz[VSA_WS_CAND_SCORE] = (size_t)BH * g.nb * 4;

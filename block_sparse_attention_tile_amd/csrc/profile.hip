@@ -9,17 +9,26 @@
 // an evenly spread set of runs of 32 consecutive raster tokens; MSE is the
 // mean over the sampled rows and channels; ties go to the lower candidate.
 //
-// profile_full_kernel: one wave per (head, run of 32 query rows) sweeps all
-// keys, line by line of the raster grid (a line = the W tokens of one
-// (t, h)), in chunks of up to 64 keys staged in LDS (K by direct loads in
-// MFMA lane order, V transposed through VGPRs), and stores the full
-// attention outputs of the run in fp32.
-// profile_masked_kernel: one wave per (head, run, candidate) visits only the
-// lines that some row's kept keys reach.  A candidate's kept keys on a line
-// are, per query row, one interval of w (its window is a box of token
-// coordinates) plus, for every row alike, one interval of sink tiles; the
-// wave sums the squared differences of its masked outputs to the full ones.
+// Keys are visited line by line of the raster grid (a line = the W tokens of
+// one (t, h)), in chunks of up to 64 keys.  A chunk is staged in LDS by
+// direct global->LDS loads: K into the padded, lane-ordered rows the MFMA
+// core reads, V into padded natural rows, then transposed LDS to LDS into
+// the core's V^T rows (16-byte reads of 16 consecutive rows hit distinct
+// banks; 4-byte writes of consecutive key pairs are consecutive).
 //
+// profile_full_kernel: four waves (four runs of 32 sampled rows of one head)
+// share each staged chunk; the keys of a head are split into prof_segs
+// ranges of lines, one workgroup each, so the launch fills the chip.  K is
+// double-buffered: the next chunk's loads fly while the current one is
+// multiplied.  Each wave stores its unnormalised partial (O^T, row sum,
+// integer exp2 reference) per segment.
+// profile_masked_kernel: one wave per (head, run, candidate) merges the
+// segments into the full outputs (exact power-of-two rescales), then visits
+// only the lines that some row's kept keys reach.  A candidate's kept keys
+// on a line are, per query row, one interval of w (its window is a box of
+// token coordinates) plus, for every row alike, one interval of sink tiles;
+// the wave sums the squared differences of its masked outputs to the full
+// ones.
 // choose_profile_kernel: per head, the MSE of every candidate (fixed-order
 // sums over the runs) and the argmin, into the workspace's CAND /
 // CAND_SCORE regions that the layout, selection and attention read.
@@ -145,88 +154,128 @@ __device__ __forceinline__ void mask_intervals(f32x16& s, int a1, int b1, int a2
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Stage up to 64 consecutive raster keys (nk valid) into LDS.  K: direct
-// global->LDS loads into the padded, lane-ordered rows of Lds<D> (each
-// instruction fills 1 KB; rows past nk re-read row nk-1, which the masks
-// drop).  V^T: through VGPRs, one channel pair per lane (with d = 64 the two
-// lane halves split the keys), 8 keys per batch, keys past nk zero.
+constexpr int kFullWaves = 4;  // runs sharing one full-pass workgroup
+
+// LDS parts of a chunk (bf16 elements): K rows in MFMA lane order and V rows
+// in key order, both padded to D + 8 elements; V^T rows of Lds<D>.
 template <int D>
-__device__ __forceinline__ void stage_keys(uint16_t* lk, uint16_t* lvt, const uint16_t* __restrict__ k0,
-                                           const uint16_t* __restrict__ v0, int nk, int lane) {
-  constexpr int KC16 = Lds<D>::KC16;
-  constexpr int KI = kKC * (KC16 + 1) / 64;  // 1 KB instructions of the K part
+struct Chunk {
+  static constexpr int ROW = D + 8;
+  static constexpr int KE = kKC * ROW;  // == Lds<D>::KE
+  static constexpr int KC16 = D / 8;
+  static constexpr int INS = kKC * (KC16 + 1) / 64;  // 1 KB direct loads per part
+  static_assert(KE == Lds<D>::KE, "same K stage as the tile kernel");
+};
+
+// Issue the direct loads of keys [0, nk) of a chunk (rows past nk re-read row
+// nk - 1; masks drop them): K into kbuf (lane order), V into vraw (key
+// order).  The 2 * INS instructions are dealt round-robin over NW waves.
+template <int D, int NW>
+__device__ __forceinline__ void issue_chunk(uint16_t* kbuf, uint16_t* vraw, const uint16_t* __restrict__ k0,
+                                            const uint16_t* __restrict__ v0, int nk, int wave, int lane) {
+  constexpr int INS = Chunk<D>::INS, KC16 = Chunk<D>::KC16;
 #pragma unroll
-  for (int ins = 0; ins < KI; ++ins) {
-    const int u = ins * 64 + lane;
+  for (int x = 0; x < (2 * INS + NW - 1) / NW; ++x) {
+    const int ins = wave + x * NW;
+    if (ins >= 2 * INS) break;  // wave-uniform
+    const bool isv = ins >= INS;
+    const int li = isv ? ins - INS : ins;
+    const int u = li * 64 + lane;
     const int p = u / (KC16 + 1);
     const int c = min(u % (KC16 + 1), KC16 - 1);
-    const int key = min(Lds<D>::key_of_row(p), nk - 1);
-    __builtin_amdgcn_global_load_lds(k0 + (long)key * D + c * 8, (lds_ptr_t)(lk + ins * 512), 16, 0, 0);
+    const int key = min(isv ? p : Lds<D>::key_of_row(p), nk - 1);
+    __builtin_amdgcn_global_load_lds((isv ? v0 : k0) + (long)key * D + c * 8,
+                                     (lds_ptr_t)((isv ? vraw : kbuf) + li * 512), 16, 0, 0);
   }
-  constexpr int PAIRS = D / 2;
-  static_assert(PAIRS == 64 || PAIRS == 32, "d is 64 or 128");
-  constexpr int KEYS = PAIRS == 64 ? 64 : 32;  // keys handled by one lane
-  const int pp = lane % PAIRS;
-  const int k_first = (lane / PAIRS) * KEYS;
-#pragma unroll 1
-  for (int g8 = 0; g8 < KEYS / 8; ++g8) {
-    uint32_t wv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = k_first + g8 * 8 + j;
-      wv[j] = key < nk ? *reinterpret_cast<const uint32_t*>(v0 + (long)key * D + 2 * pp) : 0u;
-    }
-    uint4 lo, hv;
-    lo.x = (wv[0] & 0xffffu) | (wv[1] << 16);
-    lo.y = (wv[2] & 0xffffu) | (wv[3] << 16);
-    lo.z = (wv[4] & 0xffffu) | (wv[5] << 16);
-    lo.w = (wv[6] & 0xffffu) | (wv[7] << 16);
-    hv.x = (wv[0] >> 16) | (wv[1] & 0xffff0000u);
-    hv.y = (wv[2] >> 16) | (wv[3] & 0xffff0000u);
-    hv.z = (wv[4] >> 16) | (wv[5] & 0xffff0000u);
-    hv.w = (wv[6] >> 16) | (wv[7] & 0xffff0000u);
-    const int c = k_first / 8 + g8;
-    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp, c)) = lo;
-    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp + 1, c)) = hv;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct loads have landed
 }
 
-// Full attention of one run of 32 sampled query rows over all keys (the
-// reference outputs), written to ofull [B*H][runs][32][d] in fp32.
+// V rows (key order, padded) -> V^T rows of Lds<D>, by NT threads: each
+// work item packs one key pair of 8 channels into 8 dwords.
+template <int D, int NT>
+__device__ __forceinline__ void transpose_v(const uint16_t* vraw, uint16_t* lvt, int tid) {
+  constexpr int ITEMS = (kKC / 2) * (D / 8);
+#pragma unroll
+  for (int x = 0; x < ITEMS / NT; ++x) {
+    const int u = tid + x * NT;
+    const int m = u % (kKC / 2), c8 = u / (kKC / 2);
+    const uint4 a = *reinterpret_cast<const uint4*>(vraw + (2 * m) * Chunk<D>::ROW + c8 * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(vraw + (2 * m + 1) * Chunk<D>::ROW + c8 * 8);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint32_t*>(lvt + (c8 * 8 + 2 * j) * Lds<D>::VROW + 2 * m) =
+          (aw[j] & 0xffffu) | (bw[j] << 16);
+      *reinterpret_cast<uint32_t*>(lvt + (c8 * 8 + 2 * j + 1) * Lds<D>::VROW + 2 * m) =
+          (aw[j] >> 16) | (bw[j] & 0xffff0000u);
+    }
+  }
+}
+
+// Full attention of the sampled rows over the keys of one segment of lines:
+// four waves (runs) share each chunk; K double-buffered, V staged once per
+// chunk and transposed.  Output per (run, segment, row): the unnormalised
+// O^T registers, the row sum and the reference.
 template <int D>
-__global__ __launch_bounds__(64, 1) void profile_full_kernel(Geo g, const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ k,
-                                                            const uint16_t* __restrict__ v,
-                                                            float* __restrict__ ofull) {
-  __shared__ __align__(16) uint16_t lds[Lds<D>::STAGE];
-  uint16_t* const lk = lds;
-  uint16_t* const lvt = lds + Lds<D>::KE;
-  const int run = blockIdx.x;
-  const long bh = blockIdx.y;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kFullWaves * 64, 2) void profile_full_kernel(
+    Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    float* __restrict__ part_acc, float2* __restrict__ part_lm) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* const kbuf0 = lds;
+  uint16_t* const kbuf1 = lds + Chunk<D>::KE;
+  uint16_t* const vraw = lds + 2 * Chunk<D>::KE;
+  uint16_t* const lvt = lds + 3 * Chunk<D>::KE;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, hi = lane >> 5;
+  const int run = blockIdx.x * kFullWaves + wave;
+  const bool active = run < g.prof_runs;
+  const long bh = blockIdx.y;
+  const int seg = blockIdx.z;
   const long N = g.N;
-  const long row0 = N < kRun ? 0 : (long)run * N / g.prof_runs;
-  const long qtok = min(row0 + col, N - 1);
-  const long head = bh * N * D;
   const int W = g.grid[2];
   const long lines = (long)g.grid[0] * g.grid[1];
+  const long l0 = lines * seg / g.prof_segs, l1 = lines * (seg + 1) / g.prof_segs;
+  const int cpl = (W + kKC - 1) / kKC;
+  const long n = (l1 - l0) * cpl;
+  const long row0 = N < kRun ? 0 : (long)min(run, g.prof_runs - 1) * N / g.prof_runs;
+  const long qtok = min(row0 + col, N - 1);
+  const long head = bh * N * D;
 
   core::WaveState<D> full;
   full.init(q + head + qtok * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);
-  for (long line = 0; line < lines; ++line) {
-    for (int w0 = 0; w0 < W; w0 += kKC) {
-      const int nk = min(kKC, W - w0);
-      __syncthreads();  // the previous chunk's reads are done
-      const long key0 = line * W + w0;
-      stage_keys<D>(lk, lvt, k + head + key0 * D, v + head + key0 * D, nk, lane);
-      __syncthreads();
+  auto key0_of = [&](long i, int* nk) {
+    const long line = l0 + i / cpl;
+    const int w0 = (int)(i % cpl) * kKC;
+    *nk = min(kKC, W - w0);
+    return line * W + w0;
+  };
+  if (n > 0) {
+    int nk0;
+    const long key0 = key0_of(0, &nk0);
+    issue_chunk<D, kFullWaves>(kbuf0, vraw, k + head + key0 * D, v + head + key0 * D, nk0, wave, lane);
+  }
+  for (long i = 0; i < n; ++i) {
+    int nk;
+    key0_of(i, &nk);
+    uint16_t* const kcur = (i & 1) ? kbuf1 : kbuf0;
+    // this chunk's loads have landed for every wave, and every wave is done
+    // with the previous chunk (V^T and the other K buffer are free)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    transpose_v<D, kFullWaves * 64>(vraw, lvt, tid);
+    __syncthreads();
+    if (i + 1 < n) {
+      int nk1;
+      const long key1 = key0_of(i + 1, &nk1);
+      issue_chunk<D, kFullWaves>((i & 1) ? kbuf0 : kbuf1, vraw, k + head + key1 * D, v + head + key1 * D,
+                                 nk1, wave, lane);
+    }
+    if (active) {
       for (int kb = 0; kb < 2; ++kb) {
         const int nkb = nk - 32 * kb;
         if (nkb <= 0) break;
-        f32x16 s = full.scores(lk, kb, col, hi);
+        f32x16 s = full.scores(kcur, kb, col, hi);
         if (nkb < 32) core::WaveState<D>::mask(s, nkb, hi);
         bf16x8 pb[2];
         full.softmax(s, c2, pb);
@@ -234,36 +283,37 @@ __global__ __launch_bounds__(64, 1) void profile_full_kernel(Geo g, const uint16
       }
     }
   }
-  const float l = full.l_part + __shfl_xor(full.l_part, 32);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* out = ofull + ((bh * g.prof_runs + run) * kRun + col) * D;
+  const float lt = full.l_part + __shfl_xor(full.l_part, 32);  // every lane of the wave takes part
+  if (!active) return;
+  const long slot = ((bh * g.prof_runs + run) * g.prof_segs + seg) * kRun + col;
+  if (hi == 0) part_lm[slot] = make_float2(lt, full.mo);
+  float* out = part_acc + slot * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float4 x;
-      x.x = full.acc[dt][4 * r4 + 0] * inv;
-      x.y = full.acc[dt][4 * r4 + 1] * inv;
-      x.z = full.acc[dt][4 * r4 + 2] * inv;
-      x.w = full.acc[dt][4 * r4 + 3] * inv;
+      x.x = full.acc[dt][4 * r4 + 0];
+      x.y = full.acc[dt][4 * r4 + 1];
+      x.z = full.acc[dt][4 * r4 + 2];
+      x.w = full.acc[dt][4 * r4 + 3];
       *reinterpret_cast<float4*>(out + dt * 32 + 8 * r4 + 4 * hi) = x;
     }
 }
 
-// One candidate (blockIdx.z) on one run: the masked attention of the 32
-// rows over the keys its static mask keeps, and the sum over the rows and
-// channels of the squared difference to the full outputs.  Only lines that
-// some row's window box or the sink reaches are visited, and on each only
-// the hull of those w ranges.
+// One candidate (blockIdx.z) on one run: merge the full-pass segments of the
+// 32 rows, then the masked attention over the keys the candidate's static
+// mask keeps, and the sum over rows and channels of the squared difference.
+// Only lines that some row's window box or the sink reaches are visited,
+// and on each only the hull of those w ranges.
 template <int D>
-__global__ __launch_bounds__(64, 1) void profile_masked_kernel(Geo g, const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ v,
-                                                              const float* __restrict__ ofull,
-                                                              float* __restrict__ sse) {
-  __shared__ __align__(16) uint16_t lds[Lds<D>::STAGE];
+__global__ __launch_bounds__(64, 1) void profile_masked_kernel(
+    Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ part_acc, const float2* __restrict__ part_lm, float* __restrict__ sse) {
+  __shared__ __align__(16) uint16_t lds[2 * Chunk<D>::KE + Lds<D>::VE];
   uint16_t* const lk = lds;
-  uint16_t* const lvt = lds + Lds<D>::KE;
+  uint16_t* const vraw = lds + Chunk<D>::KE;
+  uint16_t* const lvt = lds + 2 * Chunk<D>::KE;
   const int run = blockIdx.x;
   const long bh = blockIdx.y;
   const int cand = blockIdx.z;
@@ -276,6 +326,41 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(Geo g, const uint
   const long qtok = min(row0 + col, N - 1);
   const long head = bh * N * D;
   const BlkGeo b = pick_blk(g, cand);
+
+  // full outputs of this lane's row and channels: merge of the segments
+  float of[D / 32][16];
+  {
+    const long base = (bh * g.prof_runs + run) * g.prof_segs;
+    float M = -INFINITY;
+    for (int sg = 0; sg < g.prof_segs; ++sg) M = fmaxf(M, part_lm[(base + sg) * kRun + col].y);
+    float l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) of[dt][r] = 0.f;
+    for (int sg = 0; sg < g.prof_segs; ++sg) {
+      const float2 lm = part_lm[(base + sg) * kRun + col];
+      if (lm.y == -INFINITY) continue;  // a segment that saw no key
+      const float f = __builtin_amdgcn_ldexpf(1.0f, (int)(lm.y - M));
+      l = fmaf(lm.x, f, l);
+      const float* src = part_acc + ((base + sg) * kRun + col) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 x = *reinterpret_cast<const float4*>(src + dt * 32 + 8 * r4 + 4 * hi);
+          of[dt][4 * r4 + 0] = fmaf(x.x, f, of[dt][4 * r4 + 0]);
+          of[dt][4 * r4 + 1] = fmaf(x.y, f, of[dt][4 * r4 + 1]);
+          of[dt][4 * r4 + 2] = fmaf(x.z, f, of[dt][4 * r4 + 2]);
+          of[dt][4 * r4 + 3] = fmaf(x.w, f, of[dt][4 * r4 + 3]);
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) of[dt][r] *= inv;
+  }
 
   core::WaveState<D> qs;  // Q fragments and the score product only
   qs.init(q + head + qtok * D, hi);
@@ -320,8 +405,11 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(Geo g, const uint
       const long line = ((long)t * H + h) * W;
       for (int w0 = w_lo; w0 <= w_hi; w0 += kKC) {
         const int nk = min(kKC, w_hi + 1 - w0);
+        __syncthreads();  // the previous chunk's reads are done
+        issue_chunk<D, 1>(lk, vraw, k + head + (line + w0) * D, v + head + (line + w0) * D, nk, 0, lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        stage_keys<D>(lk, lvt, k + head + (line + w0) * D, v + head + (line + w0) * D, nk, lane);
+        transpose_v<D, 64>(vraw, lvt, lane);
         __syncthreads();
         for (int kb = 0; kb < 2; ++kb) {
           const int nkb = nk - 32 * kb;
@@ -342,19 +430,13 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(Geo g, const uint
 
   const float l = acc.l_part + __shfl_xor(acc.l_part, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float* ref = ofull + ((bh * g.prof_runs + run) * kRun + col) * D;
   float e = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 x = *reinterpret_cast<const float4*>(ref + dt * 32 + 8 * r4 + 4 * hi);
-      const float d0 = acc.acc[dt][4 * r4 + 0] * inv - x.x, d1 = acc.acc[dt][4 * r4 + 1] * inv - x.y;
-      const float d2 = acc.acc[dt][4 * r4 + 2] * inv - x.z, d3 = acc.acc[dt][4 * r4 + 3] * inv - x.w;
-      e = fmaf(d0, d0, e);
-      e = fmaf(d1, d1, e);
-      e = fmaf(d2, d2, e);
-      e = fmaf(d3, d3, e);
+    for (int r = 0; r < 16; ++r) {
+      const float d = acc.acc[dt][r] * inv - of[dt][r];
+      e = fmaf(d, d, e);
     }
   if (!valid) e = 0.f;
 #pragma unroll
@@ -385,22 +467,34 @@ __global__ void choose_profile_kernel(Geo g, const float* __restrict__ sse, floa
 }
 
 // Explicit instantiations of the kernels the launcher picks.
-template __global__ void profile_full_kernel<128>(Geo, const uint16_t*, const uint16_t*, const uint16_t*, float*);
-template __global__ void profile_full_kernel<64>(Geo, const uint16_t*, const uint16_t*, const uint16_t*, float*);
+template __global__ void profile_full_kernel<128>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
+                                                  float*, float2*);
+template __global__ void profile_full_kernel<64>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
+                                                 float*, float2*);
 template __global__ void profile_masked_kernel<128>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
-                                                    const float*, float*);
+                                                    const float*, const float2*, float*);
 template __global__ void profile_masked_kernel<64>(Geo, const uint16_t*, const uint16_t*, const uint16_t*,
-                                                   const float*, float*);
+                                                   const float*, const float2*, float*);
 
 template <int D>
 hipError_t launch_profile_d(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, hipStream_t s) {
-  hipLaunchKernelGGL(profile_full_kernel<D>, dim3(g.prof_runs, g.B * g.H), dim3(64), 0, s, g, q, k, v,
-                     w.prof_ofull);
+  const size_t shmem = (size_t)(3 * Chunk<D>::KE + Lds<D>::VE) * sizeof(uint16_t);
+  static bool attr_set = false;  // more than 64 KB of dynamic LDS must be requested
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&profile_full_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  float2* part_lm = reinterpret_cast<float2*>(w.prof_part);
+  float* part_acc = w.prof_part + (size_t)g.B * g.H * g.prof_runs * g.prof_segs * kRun * 2;
+  hipLaunchKernelGGL(profile_full_kernel<D>, dim3((g.prof_runs + kFullWaves - 1) / kFullWaves, g.B * g.H, g.prof_segs),
+                     dim3(kFullWaves * 64), shmem, s, g, q, k, v, part_acc, part_lm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(profile_masked_kernel<D>, dim3(g.prof_runs, g.B * g.H, g.nb), dim3(64), 0, s, g, q,
-                     k, v, w.prof_ofull, w.prof_sse);
+                     k, v, part_acc, part_lm, w.prof_sse);
   return hipGetLastError();
 }
 

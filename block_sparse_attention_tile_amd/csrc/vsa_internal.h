@@ -36,6 +36,7 @@ struct Geo {
   int sink;         // leading key tiles kept for every query tile
   int f8;           // 1 under VSA_COMPUTE_FP8: E4M3 tile-major Q, K, V and attention
   int prof_runs;    // VSA_PROFILE_SELECT: sampled runs of 32 query rows per head
+  int prof_segs;    // key segments (ranges of raster lines) of the full pass
   // fine-grained mask
   int fine_M, fine_G;
   long fine_keep;   // kept (group, key) pairs per head (target count)
@@ -98,7 +99,8 @@ struct Ws {
   int* f8_exp;          // [B*H][3] E4M3 scale exponents of Q, K, V
   uint32_t* f8_amax;    // [B*H][3][kAmaxParts] partial max |x| (bf16 bits)
   float* prof_sse;      // [B*H][prof_runs][nb] squared-error sums of the profiling selector
-  float* prof_ofull;    // [B*H][prof_runs][32][d] full-attention outputs of the sampled rows
+  float* prof_part;     // full-pass partials: float2 (row sum, reference) [B*H][runs][segs][32],
+                        // then fp32 O^T [B*H][runs][segs][32][d]
 };
 
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.

@@ -201,7 +201,8 @@ typedef struct vsa_plan_info {
 #define VSA_WS_F8_EXP     19  /* int32 [B*H][3] exponents e_q, e_k, e_v (VSA_COMPUTE_FP8) */
 #define VSA_WS_F8_AMAX    20  /* uint32 [B*H][3][parts] partial max |x| as bf16 bits (VSA_COMPUTE_FP8) */
 #define VSA_WS_PROF_SSE   21  /* fp32 [B*H][runs][n_blockings] squared-error sums (VSA_PROFILE_SELECT) */
-#define VSA_WS_PROF_OFULL 22  /* fp32 [B*H][runs][32][d] full-attention outputs of the sampled rows */
+#define VSA_WS_PROF_PART  22  /* profiling full-pass partials per key segment: float2 [B*H][runs][segs][32]
+                                 (row sum, exp2 reference), then fp32 [B*H][runs][segs][32][d] */
 #define VSA_WS_NREGIONS   23
 /* Under VSA_COMPUTE_FP8 the QT, KT and VT regions hold E4M3 bytes in the
  * same layouts with 1-byte elements, except that inside every aligned group

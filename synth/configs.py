@@ -65,6 +65,13 @@ CONFIGS = {
                        candidates=((1, 16, 16), (7, 4, 4), (3, 8, 8)),
                        topk_frac=0.2, ell=(8.0, 1.0, 1.0),
                        ell_alt=(1.0, 8.0, 8.0)),
+    # HunyuanVideo 720p shape, per-head spatial / temporal choice by the
+    # profiling selector: whole-frame tiles (1, 48, 80) vs 4x4-position tiles
+    # across all 30 frames (30, 4, 4), each attending within its own tile;
+    # anisotropic heads as for Wan-14B.
+    "hunyuan_svg": Workload("hunyuan_svg", 1, 24, 128, (30, 48, 80), (1, 48, 80),
+                            candidates=((1, 48, 80), (30, 4, 4)), window=(1, 1, 1),
+                            selector="profile", ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0)),
     # Fine-grained M x 1 slices at the Wan-2.1-1.3B 480p shape.
     "fine": Workload("fine", 1, 12, 128, (21, 30, 52), (1, 1, 1),
                      fine_group=64, fine_keep=0.15),

@@ -214,4 +214,5 @@ def test_profile_errors_and_sizes():
                                            profile_frac=0.5))
     runs = 4  # round(0.5 * 256 / 32)
     assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_SSE)[1] == 2 * runs * 2 * 4
-    assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_OFULL)[1] == 2 * runs * 32 * 64 * 4
+    segs = min(-(-1024 // (2 * 1)), 4 * 8, 16)  # groups = B*H*ceil(runs/4) = 2; lines = 32
+    assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_PART)[1] == 2 * runs * segs * 32 * (64 + 2) * 4
