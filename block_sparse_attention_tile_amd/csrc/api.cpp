@@ -284,8 +284,8 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
         g.prof_runs = (int)std::min(std::max(r, 1L), N / 32);
       }
       // split the keys into ranges of lines until the full pass has about
-      // 1024 workgroups of four runs (two rounds of two per CU)
-      const long groups = (long)g.B * g.H * ((g.prof_runs + 3) / 4);
+      // 1024 workgroups (a few rounds over the CUs)
+      const long groups = (long)g.B * g.H * ((g.prof_runs + vsa::kProfWaves - 1) / vsa::kProfWaves);
       const long lines = (long)pr->grid[0] * pr->grid[1];
       g.prof_segs = (int)std::max(1L, std::min({(1024 + groups - 1) / groups, lines, 16L}));
     }

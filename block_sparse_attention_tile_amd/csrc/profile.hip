@@ -16,15 +16,17 @@
 // the core's V^T rows (16-byte reads of 16 consecutive rows hit distinct
 // banks; 4-byte writes of consecutive key pairs are consecutive).
 //
-// profile_full_kernel: four waves (four runs of 32 sampled rows of one head)
+// profile_full_kernel: kProfWaves waves (runs of 32 sampled rows of one head)
 // share each staged chunk; the keys of a head are split into prof_segs
-// ranges of lines, one workgroup each, so the launch fills the chip.  K is
-// double-buffered: the next chunk's loads fly while the current one is
-// multiplied.  Each wave stores its unnormalised partial (O^T, row sum,
-// integer exp2 reference) per segment.
+// ranges of lines, one workgroup each, so the launch fills the chip.  A
+// chunk is loaded two iterations ahead and transposed one ahead, with one
+// barrier per chunk.  Each wave stores its unnormalised partial (O^T, row
+// sum, integer exp2 reference) per segment.
 // profile_masked_kernel: one wave per (head, run, candidate) merges the
 // segments into the full outputs (exact power-of-two rescales), then visits
-// only the lines that some row's kept keys reach.  A candidate's kept keys
+// only the lines that some row's kept keys reach (K by direct loads, V
+// through VGPRs with every load of a chunk in flight; 35 KB of LDS, so four
+// of these latency-bound waves share a CU).  A candidate's kept keys
 // on a line are, per query row, one interval of w (its window is a box of
 // token coordinates) plus, for every row alike, one interval of sink tiles;
 // the wave sums the squared differences of its masked outputs to the full
@@ -154,7 +156,7 @@ __device__ __forceinline__ void mask_intervals(f32x16& s, int a1, int b1, int a2
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kFullWaves = 4;  // runs sharing one full-pass workgroup
+constexpr int kFullWaves = kProfWaves;  // runs sharing one full-pass workgroup
 
 // LDS parts of a chunk (bf16 elements): K rows in MFMA lane order and V rows
 // in key order, both padded to D + 8 elements; V^T rows of Lds<D>.
@@ -195,8 +197,9 @@ template <int D, int NT>
 __device__ __forceinline__ void transpose_v(const uint16_t* vraw, uint16_t* lvt, int tid) {
   constexpr int ITEMS = (kKC / 2) * (D / 8);
 #pragma unroll
-  for (int x = 0; x < ITEMS / NT; ++x) {
+  for (int x = 0; x < (ITEMS + NT - 1) / NT; ++x) {
     const int u = tid + x * NT;
+    if (ITEMS % NT != 0 && u >= ITEMS) break;
     const int m = u % (kKC / 2), c8 = u / (kKC / 2);
     const uint4 a = *reinterpret_cast<const uint4*>(vraw + (2 * m) * Chunk<D>::ROW + c8 * 8);
     const uint4 b = *reinterpret_cast<const uint4*>(vraw + (2 * m + 1) * Chunk<D>::ROW + c8 * 8);
@@ -211,19 +214,76 @@ __device__ __forceinline__ void transpose_v(const uint16_t* vraw, uint16_t* lvt,
   }
 }
 
-// Full attention of the sampled rows over the keys of one segment of lines:
-// four waves (runs) share each chunk; K double-buffered, V staged once per
-// chunk and transposed.  Output per (run, segment, row): the unnormalised
-// O^T registers, the row sum and the reference.
+// V^T of keys [0, nk) of a chunk (keys past nk zero) through VGPRs: one
+// channel pair per lane (with d = 64 the two lane halves split the keys),
+// every load of the chunk in flight at once, then 16-byte writes of 8 keys.
 template <int D>
-__global__ __launch_bounds__(kFullWaves * 64, 2) void profile_full_kernel(
+__device__ __forceinline__ void stage_v_regs(uint16_t* lvt, const uint16_t* __restrict__ v0, int nk, int lane) {
+  constexpr int PAIRS = D / 2;
+  static_assert(PAIRS == 64 || PAIRS == 32, "d is 64 or 128");
+  constexpr int KEYS = PAIRS == 64 ? 64 : 32;  // keys handled by one lane
+  const int pp = lane % PAIRS;
+  const int k_first = (lane / PAIRS) * KEYS;
+  uint32_t wv[KEYS];
+#pragma unroll
+  for (int j = 0; j < KEYS; ++j) {
+    const int key = k_first + j;
+    wv[j] = key < nk ? *reinterpret_cast<const uint32_t*>(v0 + (long)key * D + 2 * pp) : 0u;
+  }
+#pragma unroll
+  for (int g8 = 0; g8 < KEYS / 8; ++g8) {
+    const uint32_t* w8 = wv + g8 * 8;
+    uint4 lo, hv;
+    lo.x = (w8[0] & 0xffffu) | (w8[1] << 16);
+    lo.y = (w8[2] & 0xffffu) | (w8[3] << 16);
+    lo.z = (w8[4] & 0xffffu) | (w8[5] << 16);
+    lo.w = (w8[6] & 0xffffu) | (w8[7] << 16);
+    hv.x = (w8[0] >> 16) | (w8[1] & 0xffff0000u);
+    hv.y = (w8[2] >> 16) | (w8[3] & 0xffff0000u);
+    hv.z = (w8[4] >> 16) | (w8[5] & 0xffff0000u);
+    hv.w = (w8[6] >> 16) | (w8[7] & 0xffff0000u);
+    const int c = k_first / 8 + g8;
+    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp, c)) = lo;
+    *reinterpret_cast<uint4*>(lvt + Lds<D>::v_off(2 * pp + 1, c)) = hv;
+  }
+}
+
+// K of keys [0, nk) of a chunk by direct loads into lane-ordered rows (rows
+// past nk re-read row nk - 1), one wave.
+template <int D>
+__device__ __forceinline__ void issue_k(uint16_t* kbuf, const uint16_t* __restrict__ k0, int nk, int lane) {
+  constexpr int INS = Chunk<D>::INS, KC16 = Chunk<D>::KC16;
+#pragma unroll
+  for (int ins = 0; ins < INS; ++ins) {
+    const int u = ins * 64 + lane;
+    const int p = u / (KC16 + 1);
+    const int c = min(u % (KC16 + 1), KC16 - 1);
+    const int key = min(Lds<D>::key_of_row(p), nk - 1);
+    __builtin_amdgcn_global_load_lds(k0 + (long)key * D + c * 8, (lds_ptr_t)(kbuf + ins * 512), 16, 0, 0);
+  }
+}
+
+// Full attention of the sampled rows over the keys of one segment of lines:
+// kFullWaves waves (runs) share each chunk.  Three-deep pipeline with one
+// barrier per chunk: chunk j's direct loads are issued two iterations ahead
+// (K into one of three buffers, V rows into one of two), its V is
+// transposed one iteration ahead (into one of two V^T buffers), and it is
+// multiplied in iteration j.  Output per (run, segment, row): the
+// unnormalised O^T registers, the row sum and the reference.
+template <int D>
+struct FullLds {
+  static constexpr int K0 = 0;
+  static constexpr int V0 = 3 * Chunk<D>::KE;          // V rows, two buffers
+  static constexpr int T0 = V0 + 2 * Chunk<D>::KE;     // V^T, two buffers
+  static constexpr int TOTAL = T0 + 2 * Lds<D>::VE;    // elements
+};
+
+template <int D>
+__global__ __launch_bounds__(kFullWaves * 64, kFullWaves / 4) void profile_full_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ part_acc, float2* __restrict__ part_lm) {
   extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t* const kbuf0 = lds;
-  uint16_t* const kbuf1 = lds + Chunk<D>::KE;
-  uint16_t* const vraw = lds + 2 * Chunk<D>::KE;
-  uint16_t* const lvt = lds + 3 * Chunk<D>::KE;
+  using F = FullLds<D>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int col = lane & 31, hi = lane >> 5;
@@ -244,34 +304,33 @@ __global__ __launch_bounds__(kFullWaves * 64, 2) void profile_full_kernel(
   core::WaveState<D> full;
   full.init(q + head + qtok * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);
-  auto key0_of = [&](long i, int* nk) {
-    const long line = l0 + i / cpl;
-    const int w0 = (int)(i % cpl) * kKC;
-    *nk = min(kKC, W - w0);
-    return line * W + w0;
+  auto keys_of = [&](long i) { return min(kKC, W - (int)(i % cpl) * kKC); };
+  auto issue = [&](long j) {
+    const long key0 = (l0 + j / cpl) * W + (j % cpl) * kKC;
+    issue_chunk<D, kFullWaves>(lds + F::K0 + (j % 3) * Chunk<D>::KE, lds + F::V0 + (j & 1) * Chunk<D>::KE,
+                               k + head + key0 * D, v + head + key0 * D, keys_of(j), wave, lane);
   };
+  if (n > 0) issue(0);
+  if (n > 1) issue(1);
   if (n > 0) {
-    int nk0;
-    const long key0 = key0_of(0, &nk0);
-    issue_chunk<D, kFullWaves>(kbuf0, vraw, k + head + key0 * D, v + head + key0 * D, nk0, wave, lane);
-  }
-  for (long i = 0; i < n; ++i) {
-    int nk;
-    key0_of(i, &nk);
-    uint16_t* const kcur = (i & 1) ? kbuf1 : kbuf0;
-    // this chunk's loads have landed for every wave, and every wave is done
-    // with the previous chunk (V^T and the other K buffer are free)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    transpose_v<D, kFullWaves * 64>(vraw, lvt, tid);
+    transpose_v<D, kFullWaves * 64>(lds + F::V0, lds + F::T0, tid);
+  }
+  for (long i = 0; i < n; ++i) {
+    // chunk i + 1 has landed (every wave waited for its own loads) and its
+    // V buffer is free to transpose; chunk i's V^T is complete; everything
+    // chunk i - 1 read is free
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (i + 1 < n) {
-      int nk1;
-      const long key1 = key0_of(i + 1, &nk1);
-      issue_chunk<D, kFullWaves>((i & 1) ? kbuf0 : kbuf1, vraw, k + head + key1 * D, v + head + key1 * D,
-                                 nk1, wave, lane);
-    }
+    if (i + 2 < n) issue(i + 2);
+    if (i + 1 < n)
+      transpose_v<D, kFullWaves * 64>(lds + F::V0 + ((i + 1) & 1) * Chunk<D>::KE,
+                                      lds + F::T0 + ((i + 1) & 1) * Lds<D>::VE, tid);
     if (active) {
+      const uint16_t* kcur = lds + F::K0 + (i % 3) * Chunk<D>::KE;
+      const uint16_t* vcur = lds + F::T0 + (i & 1) * Lds<D>::VE;
+      const int nk = keys_of(i);
       for (int kb = 0; kb < 2; ++kb) {
         const int nkb = nk - 32 * kb;
         if (nkb <= 0) break;
@@ -279,7 +338,7 @@ __global__ __launch_bounds__(kFullWaves * 64, 2) void profile_full_kernel(
         if (nkb < 32) core::WaveState<D>::mask(s, nkb, hi);
         bf16x8 pb[2];
         full.softmax(s, c2, pb);
-        full.pv(lvt, kb, col, hi, pb);
+        full.pv(vcur, kb, col, hi, pb);
       }
     }
   }
@@ -301,25 +360,73 @@ __global__ __launch_bounds__(kFullWaves * 64, 2) void profile_full_kernel(
     }
 }
 
+// The chunks a candidate visits for one run (wave-uniform): the lines that
+// some row's window box (hull ulo..uhi) or the sink reaches, on each the hull
+// of those w ranges, in steps of 64 keys.
+struct MaskedChunks {
+  int t, h, w0, w_hi, sink_end;
+  bool valid;
+
+  __device__ __forceinline__ bool line_at(const Geo& g, const BlkGeo& b, const int ulo[3],
+                                          const int uhi[3]) {
+    const int W = g.grid[2];
+    const bool box_line = t >= ulo[0] && t <= uhi[0] && h >= ulo[1] && h <= uhi[1];
+    // sink tiles on this line: tile index base + w / tw < sink
+    const int base = ((t / b.tile[0]) * b.nt[1] + h / b.tile[1]) * b.nt[2];
+    const int ms = g.sink - base;
+    sink_end = ms > 0 ? (int)min((long)ms * b.tile[2], (long)W) : 0;  // w < sink_end
+    if (!box_line && sink_end == 0) return false;
+    w0 = box_line ? ulo[2] : W;
+    w_hi = box_line ? uhi[2] : -1;
+    if (sink_end > 0) {
+      w0 = 0;
+      w_hi = max(w_hi, sink_end - 1);
+    }
+    return true;
+  }
+  // from line (t, h) on, the first line that is visited
+  __device__ __forceinline__ void seek(const Geo& g, const BlkGeo& b, const int ulo[3], const int uhi[3]) {
+    for (; t < g.grid[0]; ++t, h = 0)
+      for (; h < g.grid[1]; ++h)
+        if (line_at(g, b, ulo, uhi)) {
+          valid = true;
+          return;
+        }
+    valid = false;
+  }
+  __device__ __forceinline__ void start(const Geo& g, const BlkGeo& b, const int ulo[3], const int uhi[3]) {
+    t = 0;
+    h = 0;
+    seek(g, b, ulo, uhi);
+  }
+  __device__ __forceinline__ void next(const Geo& g, const BlkGeo& b, const int ulo[3], const int uhi[3]) {
+    w0 += kKC;
+    if (w0 <= w_hi) return;
+    if (++h == g.grid[1]) {
+      h = 0;
+      ++t;
+    }
+    seek(g, b, ulo, uhi);
+  }
+  __device__ __forceinline__ int keys() const { return min(kKC, w_hi + 1 - w0); }
+};
+
 // One candidate (blockIdx.z) on one run: merge the full-pass segments of the
 // 32 rows, then the masked attention over the keys the candidate's static
 // mask keeps, and the sum over rows and channels of the squared difference.
-// Only lines that some row's window box or the sink reaches are visited,
-// and on each only the hull of those w ranges.
 template <int D>
 __global__ __launch_bounds__(64, 1) void profile_masked_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ part_acc, const float2* __restrict__ part_lm, float* __restrict__ sse) {
-  __shared__ __align__(16) uint16_t lds[2 * Chunk<D>::KE + Lds<D>::VE];
+  __shared__ __align__(16) uint16_t lds[Chunk<D>::KE + Lds<D>::VE];
   uint16_t* const lk = lds;
-  uint16_t* const vraw = lds + Chunk<D>::KE;
-  uint16_t* const lvt = lds + 2 * Chunk<D>::KE;
+  uint16_t* const lvt = lds + Chunk<D>::KE;
   const int run = blockIdx.x;
   const long bh = blockIdx.y;
   const int cand = blockIdx.z;
   const int lane = threadIdx.x;
   const int col = lane & 31, hi = lane >> 5;
-  const int T = g.grid[0], H = g.grid[1], W = g.grid[2];
+  const int H = g.grid[1], W = g.grid[2];
   const long N = g.N;
   const long row0 = N < kRun ? 0 : (long)run * N / g.prof_runs;
   const bool valid = row0 + col < N;
@@ -386,45 +493,30 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(
   }
   const float c2 = (float)(g.scale * 1.4426950408889634);
 
-  for (int t = 0; t < T; ++t) {
-    for (int h = 0; h < H; ++h) {
-      const bool box_line = t >= ulo[0] && t <= uhi[0] && h >= ulo[1] && h <= uhi[1];
-      // sink tiles on this line: tile index base + w / tw < sink
-      const int base = ((t / b.tile[0]) * b.nt[1] + h / b.tile[1]) * b.nt[2];
-      const int ms = g.sink - base;
-      const int sink_end = ms > 0 ? (int)min((long)ms * b.tile[2], (long)W) : 0;  // w < sink_end
-      if (!box_line && sink_end == 0) continue;
-      int w_lo = box_line ? ulo[2] : W, w_hi = box_line ? uhi[2] : -1;
-      if (sink_end > 0) {
-        w_lo = 0;
-        w_hi = max(w_hi, sink_end - 1);
-      }
-      // this row's interval on the line (box) and the line's sink interval
-      const bool in = t >= blo[0] && t <= bhi[0] && h >= blo[1] && h <= bhi[1];
-      const int ba = in ? blo[2] : 1, bb = in ? bhi[2] : 0;
-      const long line = ((long)t * H + h) * W;
-      for (int w0 = w_lo; w0 <= w_hi; w0 += kKC) {
-        const int nk = min(kKC, w_hi + 1 - w0);
-        __syncthreads();  // the previous chunk's reads are done
-        issue_chunk<D, 1>(lk, vraw, k + head + (line + w0) * D, v + head + (line + w0) * D, nk, 0, lane);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        transpose_v<D, 64>(vraw, lvt, lane);
-        __syncthreads();
-        for (int kb = 0; kb < 2; ++kb) {
-          const int nkb = nk - 32 * kb;
-          if (nkb <= 0) break;
-          const int lo_k = w0 + 32 * kb, hi_k = lo_k + min(nkb, 32) - 1;  // w of the block's keys
-          const int a1 = max(ba, lo_k), b1 = min(bb, hi_k);
-          const int a2 = lo_k, b2 = min(sink_end - 1, hi_k);
-          if (!__any(a1 <= b1 || a2 <= b2)) continue;  // no row keeps a key of this block
-          f32x16 s = qs.scores(lk, kb, col, hi);
-          mask_intervals(s, a1 - lo_k, b1 - lo_k, a2 - lo_k, b2 - lo_k, hi);
-          bf16x8 pb[2];
-          acc.softmax(s, c2, pb);
-          acc.pv(lvt, kb, col, hi, pb);
-        }
-      }
+  MaskedChunks cur;
+  for (cur.start(g, b, ulo, uhi); cur.valid; cur.next(g, b, ulo, uhi)) {
+    const int nk = cur.keys();
+    const long key0 = ((long)cur.t * H + cur.h) * W + cur.w0;
+    __syncthreads();  // the previous chunk's reads are done
+    issue_k<D>(lk, k + head + key0 * D, nk, lane);
+    stage_v_regs<D>(lvt, v + head + key0 * D, nk, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K loads have landed
+    __syncthreads();
+    // this row's interval on the line (box) and the line's sink interval
+    const bool in = cur.t >= blo[0] && cur.t <= bhi[0] && cur.h >= blo[1] && cur.h <= bhi[1];
+    const int ba = in ? blo[2] : 1, bb = in ? bhi[2] : 0;
+    for (int kb = 0; kb < 2; ++kb) {
+      const int nkb = nk - 32 * kb;
+      if (nkb <= 0) break;
+      const int lo_k = cur.w0 + 32 * kb, hi_k = lo_k + min(nkb, 32) - 1;  // w of the block's keys
+      const int a1 = max(ba, lo_k), b1 = min(bb, hi_k);
+      const int a2 = lo_k, b2 = min(cur.sink_end - 1, hi_k);
+      if (!__any(a1 <= b1 || a2 <= b2)) continue;  // no row keeps a key of this block
+      f32x16 s = qs.scores(lk, kb, col, hi);
+      mask_intervals(s, a1 - lo_k, b1 - lo_k, a2 - lo_k, b2 - lo_k, hi);
+      bf16x8 pb[2];
+      acc.softmax(s, c2, pb);
+      acc.pv(lvt, kb, col, hi, pb);
     }
   }
 
@@ -479,7 +571,7 @@ template __global__ void profile_masked_kernel<64>(Geo, const uint16_t*, const u
 template <int D>
 hipError_t launch_profile_d(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, hipStream_t s) {
-  const size_t shmem = (size_t)(3 * Chunk<D>::KE + Lds<D>::VE) * sizeof(uint16_t);
+  const size_t shmem = (size_t)FullLds<D>::TOTAL * sizeof(uint16_t);
   static bool attr_set = false;  // more than 64 KB of dynamic LDS must be requested
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&profile_full_kernel<D>),

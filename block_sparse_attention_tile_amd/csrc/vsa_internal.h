@@ -103,6 +103,10 @@ struct Ws {
                         // then fp32 O^T [B*H][runs][segs][32][d]
 };
 
+// Runs of sampled query rows (waves) sharing one workgroup of the profiling
+// selector's full pass.
+constexpr int kProfWaves = 12;
+
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.
 constexpr int kAmaxParts = 32;
 
