@@ -206,6 +206,13 @@ def main():
     if not f8 and not wl.fine_group and not args.no_fp8_leg:
         fp8_leg = _fp8_leg(wl, q, k, v, o, n_st, stage, flops)
 
+    choice = None
+    if wl.candidates:  # heads per chosen blocking (SICS or profiling selector)
+        import numpy as np
+        _, _, cand = plan.read_selection()
+        counts = np.bincount(np.asarray(cand), minlength=len(wl.candidates))
+        choice = {"x".join(map(str, c)): int(n) for c, n in zip(wl.candidates, counts)}
+
     cpu = None
     if args.cpu_budget > 0 and not wl.fine_group and not wl.candidates and not f8:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -233,6 +240,7 @@ def main():
         "stages_ms": {"layout": round(ms_layout, 4), "select": round(ms_select, 4),
                       "attend": round(ms_attend, 4)},
         "ms_per_call_cached_mask": round(ms_cached, 4),
+        "heads_per_blocking": choice,
         "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1) if bytes_layout else None,
         "layout_hbm_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                             if bytes_layout else None),
