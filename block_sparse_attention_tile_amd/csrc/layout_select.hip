@@ -104,7 +104,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // (slice, head, tensor); slice p covers a contiguous 1/kAmaxParts of the
 // head's N*d raster values.  Integer maxima of the magnitude bits order
 // finite bf16 values exactly; no atomics, so the result is deterministic.
-constexpr int kAmaxThreads = 256;
+constexpr int kAmaxThreads = 512;
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(Geo g, const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
@@ -191,7 +191,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     uint32_t m3[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      uint32_t m = lane < kAmaxParts ? f8_amax[(bh * 3 + x) * kAmaxParts + lane] : 0u;
+      uint32_t m = 0u;
+      for (int y = lane; y < kAmaxParts; y += 64) m = max(m, f8_amax[(bh * 3 + x) * kAmaxParts + y]);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
       m3[x] = m;

@@ -108,7 +108,7 @@ struct Ws {
 constexpr int kProfWaves = 12;
 
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.
-constexpr int kAmaxParts = 32;
+constexpr int kAmaxParts = 128;
 
 // Bytes of internal scratch the fine-grained mask needs (fine.hip).
 size_t fine_scratch_bytes(const Geo& g);

@@ -150,10 +150,10 @@ def test_plan_errors():
 
 
 def test_fp8_workspace_regions():
-    # E4M3 exponents [B*H][3] and partial maxima [B*H][3][32]; the bf16 plan has neither
+    # E4M3 exponents [B*H][3] and partial maxima [B*H][3][128]; the bf16 plan has neither
     prob = vsa.make_problem(2, 3, 128, (4, 8, 8), (2, 4, 4))
     for compute, want_exp, want_amax in ((vsa.VSA_COMPUTE_BF16, 0, 0),
-                                         (vsa.VSA_COMPUTE_FP8, 6 * 3 * 4, 6 * 3 * 32 * 4)):
+                                         (vsa.VSA_COMPUTE_FP8, 6 * 3 * 4, 6 * 3 * 128 * 4)):
         h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), compute=compute))
         assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_EXP)[1] == want_exp
         assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_AMAX)[1] == want_amax
