@@ -116,7 +116,7 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU: every stage is independent per (batch, head), so N GPUs would each take H/N heads with no exchange; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
