@@ -277,3 +277,30 @@ def test_fp8_hunyuan_full_size_sampled():
         tiles = sorted(set(rng.choice(nT, 3, replace=False).tolist()) | {0, nT - 1, 155})
         _check_head(o[0, h].float().cpu().numpy(), qn, kn, vn, mem, want, tiles,
                     1.0 / math.sqrt(wl.d), ("hunyuan", h))
+
+
+def test_fp8_wan14b_full_size_sampled():
+    """Wan-14B 720p shape in E4M3: per-head SICS blocking and Top-K 20%
+    selection (bit-exact, as for bf16), sampled query tiles of O for one head
+    of each blocking."""
+    wl = CONFIGS["wan14b"].with_(compute="fp8")
+    _say("fp8 wan14b full size")
+    q, k, v = _inputs(wl)
+    plan = vsa.Plan(*structs_of(wl))
+    o = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    row_ptr, col, cand = plan.read_selection()
+    rng = np.random.default_rng(1)
+    for h in (0, 1):  # the two anisotropic head kinds
+        qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
+        c, _ = oracle_candidate(wl, qn, kn)
+        assert int(cand[h]) == c
+        tile = wl.candidates[c]
+        rows, margins, mem = oracle_tile_rows(wl, qn, kn, tile)
+        got = csr_rows(row_ptr, col, h, plan.info.max_tiles, len(mem))
+        tiles = sorted(set(rng.choice(len(mem), 3, replace=False).tolist()) | {0, len(mem) - 1})
+        for i in tiles:
+            if margins[i] > 1e-9:
+                assert got[i] == rows[i], (h, i)
+        _check_head(o[0, h].float().cpu().numpy(), qn, kn, vn, mem, got, tiles, 1.0 / math.sqrt(wl.d),
+                    ("wan14b", h))

@@ -119,3 +119,37 @@ def test_planted_spatial_and_temporal_heads():
                for x in range(3))
     assert _check_plan(wl, q, k, v) == [0, 1]
 
+
+
+def test_profile_hunyuan_full_size_sampled():
+    """HunyuanVideo 720p shape with the spatial / temporal candidates: the
+    MSEs and choice of two heads (one of each field kind) against the
+    oracle over the same 1% sample, and sampled query tiles of O."""
+    from synth import CONFIGS
+    wl = CONFIGS["hunyuan_svg"]
+    _say("profile hunyuan_svg full size")
+    q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=0, device="cuda")
+    plan = vsa.Plan(*structs_of(wl))
+    o = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    nb = len(wl.candidates)
+    mse = plan.region(_lib.VSA_WS_CAND_SCORE, torch.float32).view(wl.H, nb).cpu().numpy()
+    row_ptr, col, cand = plan.read_selection()
+    for h in (0, 1):
+        qn, kn, vn = (t[0, h].float().cpu().numpy() for t in (q, k, v))
+        want = profile.profile_mse(qn, kn, vn, wl.grid, wl.candidates, wl.window, wl.win_mode, wl.sink, 0.01)
+        delta = 2.0 ** -7 * np.abs(vn).max()
+        tol = 2.0 * np.sqrt(want) * delta + delta ** 2
+        assert np.all(np.abs(mse[h] - want) <= tol), (h, mse[h], want, tol)
+        c = int(cand[h])
+        if abs(want[0] - want[1]) > 2.0 * tol.max():
+            assert c == profile.choose(want), (h, c, want)
+        tile = wl.candidates[c]
+        mem = geometry.tile_members(wl.grid, tile)
+        rows = profile.candidate_rows(wl.grid, tile, wl.window, wl.win_mode, wl.sink)
+        assert csr_rows(row_ptr, col, h, plan.info.max_tiles, len(mem)) == rows
+        tiles = [0, len(mem) // 2, len(mem) - 1]
+        ref = attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=tiles)
+        on = o[0, h].float().cpu().numpy()
+        for i in tiles:
+            assert np.abs(on[mem[i]] - ref[mem[i]]).max() <= ATOL, (h, i)
