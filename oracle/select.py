@@ -21,8 +21,8 @@ tokens):
   * "max":    S_ij = scale * <mean_i(Q), max_j(K)>;
   * "minmax": S_ij = scale * sum_c max(q_ic max_j(K)_c, q_ic min_j(K)_c), an
     upper bound of scale * <q_i, k> over the keys k of tile j.
-An attention sink (the ledger's free parameter "attention-sink length", no
-value given) keeps key tiles 0 .. sink-1 for every query tile.
+An attention sink (its length is a free parameter of the SPADE ledger, left
+without a value there) keeps key tiles 0 .. sink-1 for every query tile.
 
 Arithmetic fixed here so that an independent implementation reaches the
 same integers:
