@@ -174,3 +174,44 @@ def test_hunyuan_full_size_sampled():
         for i in tiles:
             err = np.abs(on[mem[i]] - ref[mem[i]]).max()
             assert err <= ATOL, (h, i, err)
+
+
+def test_wan480_full_size_sampled():
+    """Wan-2.1 480p shape (window 3x3x3 united with Top-P 0.9; 144-token tiles,
+    the last W tile of every row half full): pooled means and the kept tiles
+    of every head against the oracle (bit-exact; a row whose Top-P cut sits
+    within the margin of the oracle's rounding is counted, not compared),
+    and O on sampled query tiles of three heads, partial tiles included."""
+    wl = CONFIGS["wan480"]
+    _say("wan480 full size")
+    q, k, v = _inputs(wl)
+    plan, o = _run_all(wl, q, k, v)
+    row_ptr, col, _ = plan.read_selection()
+    nT = plan.info.n_tiles[0]
+    mem = geometry.tile_members(wl.grid, wl.tile)
+    assert nT == len(mem) == 245
+    pq = plan.region(_lib.VSA_WS_POOLED_Q, torch.float32).view(wl.H, nT, wl.d).cpu().numpy()
+    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.H, nT, wl.d).cpu().numpy()
+    rng = np.random.default_rng(1)
+    near_cut = 0
+    for h in range(wl.H):
+        qn, kn = (t[0, h].float().cpu().numpy() for t in (q, k))
+        assert np.array_equal(pq[h], select.pooled_means(qn, mem)), h
+        assert np.array_equal(pk[h], select.pooled_means(kn, mem)), h
+        rows, margins, _ = oracle_tile_rows(wl, qn, kn, wl.tile)
+        got = csr_rows(row_ptr, col, h, plan.info.max_tiles, nT)
+        for i in range(nT):
+            if margins[i] > 1e-9:
+                assert got[i] == rows[i], (h, i)
+            else:
+                near_cut += 1
+        if h in (0, 5, 11):
+            vn = v[0, h].float().cpu().numpy()
+            on = o[0, h].float().cpu().numpy()
+            # tile 6 and 244 are partial (4 of 8 W columns); 122 is interior
+            tiles = sorted(set(rng.choice(nT, 4, replace=False).tolist()) | {0, 6, 122, nT - 1})
+            ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+            for i in tiles:
+                err = np.abs(on[mem[i]] - ref[mem[i]]).max()
+                assert err <= ATOL, (h, i, err)
+    assert near_cut <= nT * wl.H // 100, near_cut
