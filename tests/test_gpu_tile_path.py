@@ -215,3 +215,41 @@ def test_wan480_full_size_sampled():
                 err = np.abs(on[mem[i]] - ref[mem[i]]).max()
                 assert err <= ATOL, (h, i, err)
     assert near_cut <= nT * wl.H // 100, near_cut
+
+
+MAXIMA = {
+    # 4096 tiles (the plan's limit) of one token each: the selection sorts
+    # 4096 scores per row; every key tile is a 32-slot chunk with one key
+    "max_tiles_topk": Workload("max_tiles_topk", 1, 1, 64, (16, 16, 16), (1, 1, 1), window=(3, 3, 3),
+                               topk=8),
+    "max_tiles_topp": Workload("max_tiles_topp", 1, 1, 64, (16, 16, 16), (1, 1, 1), topp=0.3),
+    # two tiles of 4096 tokens (the tile-size limit): 128 slabs per tile, so
+    # eleven workgroups of twelve waves per tile, the last with four idle waves
+    "max_tile": Workload("max_tile", 1, 1, 128, (16, 16, 32), (16, 16, 16), window=(1, 1, 3)),
+}
+
+
+@pytest.mark.parametrize("name", list(MAXIMA))
+def test_maximum_sizes(name):
+    """The limits the plan accepts: the kept tiles of every row bit-exact and
+    O within 2e-2 on every query row (sampled query tiles for the 4096-tile
+    cases)."""
+    wl = MAXIMA[name]
+    _say(f"maximum {name}")
+    q, k, v = _inputs(wl)
+    plan, o = _run_all(wl, q, k, v)
+    row_ptr, col, _ = plan.read_selection()
+    qn, kn, vn = (t[0, 0].float().cpu().numpy() for t in (q, k, v))
+    rows, margins, mem = oracle_tile_rows(wl, qn, kn, wl.tile)
+    nT = len(mem)
+    assert plan.info.n_tiles[0] == nT
+    got = csr_rows(row_ptr, col, 0, plan.info.max_tiles, nT)
+    for i in range(nT):
+        if margins[i] > 1e-9:
+            assert got[i] == rows[i], i
+    tiles = list(range(nT)) if nT <= 2 else sorted(set(range(0, nT, 37)) | {nT - 1})
+    ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+    on = o[0, 0].float().cpu().numpy()
+    for i in tiles:
+        err = np.abs(on[mem[i]] - ref[mem[i]]).max()
+        assert err <= ATOL, (i, err)
