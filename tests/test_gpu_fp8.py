@@ -57,6 +57,11 @@ CASES = {
     "sics": Workload("sics", 1, 4, 128, (14, 16, 16), (1, 16, 16),
                      candidates=((1, 16, 16), (7, 4, 4), (7, 8, 8)), topk_frac=0.2,
                      ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0), compute="fp8"),
+    # eight-wave and seven-wave workgroups (4-stage ring); the second ragged on every axis
+    "eight_slab": Workload("eight_slab", 1, 2, 128, (4, 16, 32), (1, 16, 16), window=(3, 1, 1), topk=2,
+                           compute="fp8"),
+    "seven_slab_ragged": Workload("seven_slab_ragged", 1, 2, 64, (5, 9, 30), (2, 8, 14), topp=0.9,
+                                  compute="fp8"),
 }
 
 

@@ -41,6 +41,10 @@ SMALL = {
                                  topp=0.9, summarizer="minmax", sink=2),
     # static window + sink (the plan's static counts include the sink)
     "window_sink": Workload("window_sink", 1, 2, 128, (12, 16, 24), (6, 8, 8), window=(1, 1, 3), sink=4),
+    # eight 32-row slabs per tile (eight-wave workgroups, 4-stage ring), window + Top-K
+    "eight_slab": Workload("eight_slab", 1, 2, 128, (4, 16, 32), (1, 16, 16), window=(3, 1, 1), topk=2),
+    # seven slabs (224-token tiles), ragged on every axis, Top-P, d=64
+    "seven_slab_ragged": Workload("seven_slab_ragged", 1, 2, 64, (5, 9, 30), (2, 8, 14), topp=0.9),
 }
 
 
