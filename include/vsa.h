@@ -236,6 +236,13 @@ int vsa_workspace_region(const vsa_plan_t* plan, int region, size_t* offset, siz
  * workspace (>= vsa_workspace_bytes, 256-byte aligned) is owned by the
  * caller and must not be shared by calls that overlap in time.
  *
+ * Stream capture: the calls enqueue kernel launches only (no memset, copy
+ * or allocation), so a captured graph replays them.  The first call of a
+ * kernel variant in a process also raises that kernel's dynamic-LDS limit
+ * (a host-side function attribute): make one uncaptured call with the plan
+ * before capturing.  A replay reads the buffers captured, so new inputs go
+ * into those buffers.
+ *
  * vsa_forward = vsa_layout + vsa_select + vsa_attend.  o receives the
  * attention output in the same raster layout as q. */
 int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
