@@ -352,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 #define VSA_ATTEND_INST_C(C)                                                               \
   VSA_ATTEND_INST(C, 1, 2) VSA_ATTEND_INST(C, 2, 2) VSA_ATTEND_INST(C, 3, 2)    \
   VSA_ATTEND_INST(C, 4, 2) VSA_ATTEND_INST(C, 5, 2) VSA_ATTEND_INST(C, 6, 2)    \
-  VSA_ATTEND_INST(C, 7, 4) VSA_ATTEND_INST(C, 8, 4) VSA_ATTEND_INST(C, 9, 4)    \
+  VSA_ATTEND_INST(C, 7, 2) VSA_ATTEND_INST(C, 8, 2) VSA_ATTEND_INST(C, 7, 4) VSA_ATTEND_INST(C, 8, 4) VSA_ATTEND_INST(C, 9, 4)    \
   VSA_ATTEND_INST(C, 10, 4) VSA_ATTEND_INST(C, 11, 4) VSA_ATTEND_INST(C, 12, 4)
 VSA_ATTEND_INST_C(Bf16Core<128>)
 VSA_ATTEND_INST_C(Bf16Core<64>)
@@ -390,9 +390,11 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
                     hipStream_t s) {
   // Waves per workgroup: the tile's 32-row slabs split into as few balanced
   // groups of at most kMaxWaves as possible.  At 3 waves per SIMD a CU holds
-  // 12 waves, so groups of 7 to 12 waves run one workgroup per CU and get a
-  // 4-stage ring; smaller groups run two workgroups per CU with 2 stages
-  // each.
+  // 12 waves, so groups of 7 to 12 waves run one workgroup per CU; groups of
+  // 9 to 12 get a 4-stage ring, smaller groups 2 stages (two workgroups per
+  // CU up to 6 waves).  Seven- and eight-wave E4M3 groups also get 4 stages
+  // (measured: 3% faster at Wan-14B; for bf16 the deeper ring was no faster
+  // there and 3% slower on short rows).
   const int slabs = g.blk[blocking].slots / 32;
   const int groups = (slabs + kMaxWaves - 1) / kMaxWaves;
   const int nw = (slabs + groups - 1) / groups;
@@ -403,8 +405,8 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
     case 4: return launch_one<C, 4, 2>(g, w, blocking, cand, o, s);
     case 5: return launch_one<C, 5, 2>(g, w, blocking, cand, o, s);
     case 6: return launch_one<C, 6, 2>(g, w, blocking, cand, o, s);
-    case 7: return launch_one<C, 7, 4>(g, w, blocking, cand, o, s);
-    case 8: return launch_one<C, 8, 4>(g, w, blocking, cand, o, s);
+    case 7: return C::kF8 ? launch_one<C, 7, 4>(g, w, blocking, cand, o, s) : launch_one<C, 7, 2>(g, w, blocking, cand, o, s);
+    case 8: return C::kF8 ? launch_one<C, 8, 4>(g, w, blocking, cand, o, s) : launch_one<C, 8, 2>(g, w, blocking, cand, o, s);
     case 9: return launch_one<C, 9, 4>(g, w, blocking, cand, o, s);
     case 10: return launch_one<C, 10, 4>(g, w, blocking, cand, o, s);
     case 11: return launch_one<C, 11, 4>(g, w, blocking, cand, o, s);

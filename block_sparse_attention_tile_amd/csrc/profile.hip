@@ -9,8 +9,9 @@
 // an evenly spread set of runs of 32 consecutive raster tokens; MSE is the
 // mean over the sampled rows and channels; ties go to the lower candidate.
 //
-// Keys are visited line by line of the raster grid (a line = the W tokens of
-// one (t, h)), in chunks of up to 64 keys.  A chunk is staged in LDS by
+// The full pass visits a segment's keys (a range of whole lines of the
+// raster grid, a line = the W tokens of one (t, h)) in chunks of 64
+// consecutive keys; the masked pass visits them line by line.  A chunk is staged in LDS by
 // direct global->LDS loads: K into the padded, lane-ordered rows the MFMA
 // core reads, V into padded natural rows, then transposed LDS to LDS into
 // the core's V^T rows (16-byte reads of 16 consecutive rows hit distinct
@@ -295,8 +296,10 @@ __global__ __launch_bounds__(kFullWaves * 64, kFullWaves / 4) void profile_full_
   const int W = g.grid[2];
   const long lines = (long)g.grid[0] * g.grid[1];
   const long l0 = lines * seg / g.prof_segs, l1 = lines * (seg + 1) / g.prof_segs;
-  const int cpl = (W + kKC - 1) / kKC;
-  const long n = (l1 - l0) * cpl;
+  // the segment's keys are the contiguous raster range [l0 * W, l1 * W):
+  // chunks of 64 run across line ends, so only the segment's last is partial
+  const long seg_keys = (l1 - l0) * W;
+  const long n = (seg_keys + kKC - 1) / kKC;
   const long row0 = N < kRun ? 0 : (long)min(run, g.prof_runs - 1) * N / g.prof_runs;
   const long qtok = min(row0 + col, N - 1);
   const long head = bh * N * D;
@@ -304,9 +307,9 @@ __global__ __launch_bounds__(kFullWaves * 64, kFullWaves / 4) void profile_full_
   core::WaveState<D> full;
   full.init(q + head + qtok * D, hi);
   const float c2 = (float)(g.scale * 1.4426950408889634);
-  auto keys_of = [&](long i) { return min(kKC, W - (int)(i % cpl) * kKC); };
+  auto keys_of = [&](long i) { return (int)min((long)kKC, seg_keys - i * kKC); };
   auto issue = [&](long j) {
-    const long key0 = (l0 + j / cpl) * W + (j % cpl) * kKC;
+    const long key0 = l0 * W + j * kKC;
     issue_chunk<D, kFullWaves>(lds + F::K0 + (j % 3) * Chunk<D>::KE, lds + F::V0 + (j & 1) * Chunk<D>::KE,
                                k + head + key0 * D, v + head + key0 * D, keys_of(j), wave, lane);
   };
