@@ -30,6 +30,13 @@ def oracle_tile_rows(wl, q_h, k_h, tile):
     return rows, margins, mem
 
 
+def unambiguous(tiles, margins):
+    """The query tiles whose oracle selection is unique (no Top-P cut within
+    1e-9 of the mass the oracle's rounding could move): only these are
+    compared bit-exactly, and their O against the oracle's own kept tiles."""
+    return [int(i) for i in tiles if margins[i] > 1e-9]
+
+
 def csr_rows(row_ptr, col, bh, max_tiles, n_tiles):
     base = bh * max_tiles
     return [col[row_ptr[base + i]:row_ptr[base + i + 1]].tolist() for i in range(n_tiles)]

@@ -83,7 +83,7 @@ def test_sics_choice_selection_attention(name):
             rows, tmarg, mem = oracle_tile_rows(wl, qn[b, h], kn[b, h], tile)
             got = csr_rows(row_ptr, col, bh, mt, len(mem))
             assert got == rows, (b, h)
-            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, got)
+            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, rows)
             err = np.abs(on[b, h] - ref).max()
             assert err <= ATOL, (b, h, err)
     print(f"chosen blockings {chosen}, min score margin {min(margins):.3e}", flush=True)
@@ -117,7 +117,7 @@ def test_wan14b_full_size():
         assert all(len(r) == plan.info.topk[c] for r in got)
         on = o[0, h].float().cpu().numpy()
         tiles = sorted(set(rng.choice(len(mem), 4, replace=False).tolist()) | {len(mem) - 1})
-        ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+        ref = attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=tiles)
         for i in tiles:
             err = np.abs(on[mem[i]] - ref[mem[i]]).max()
             assert err <= ATOL, (h, i, err)

@@ -12,7 +12,7 @@ import block_sparse_attention_tile_amd as vsa
 from block_sparse_attention_tile_amd import _lib
 from oracle import attention, geometry, layout, select
 from synth import CONFIGS, Workload, smooth_field_qkv
-from tests.helpers import csr_rows, oracle_tile_rows, structs_of
+from tests.helpers import csr_rows, oracle_tile_rows, structs_of, unambiguous
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-2
@@ -130,12 +130,13 @@ def test_selection_and_attention_small(name):
             bh = b * wl.H + h
             rows, margins, mem = oracle_tile_rows(wl, qn[b, h], kn[b, h], wl.tile)
             got = csr_rows(row_ptr, col, bh, plan.info.max_tiles, nT)
-            for i in range(nT):
-                if margins[i] > 1e-9:
-                    assert got[i] == rows[i], (b, h, i)
-            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, got)
-            err = np.abs(on[b, h] - ref).max()
-            assert err <= ATOL, (b, h, err)
+            ok = unambiguous(range(nT), margins)
+            for i in ok:
+                assert got[i] == rows[i], (b, h, i)
+            ref = attention.block_sparse_attention(qn[b, h], kn[b, h], vn[b, h], mem, rows, query_tiles=ok)
+            for i in ok:
+                err = np.abs(on[b, h][mem[i]] - ref[mem[i]]).max()
+                assert err <= ATOL, (b, h, i, err)
 
 
 def test_forward_is_deterministic_and_stage_split_matches():
@@ -204,17 +205,17 @@ def test_wan480_full_size_sampled():
         assert np.array_equal(pk[h], select.pooled_means(kn, mem)), h
         rows, margins, _ = oracle_tile_rows(wl, qn, kn, wl.tile)
         got = csr_rows(row_ptr, col, h, plan.info.max_tiles, nT)
-        for i in range(nT):
-            if margins[i] > 1e-9:
-                assert got[i] == rows[i], (h, i)
-            else:
-                near_cut += 1
+        ok = unambiguous(range(nT), margins)
+        near_cut += nT - len(ok)
+        for i in ok:
+            assert got[i] == rows[i], (h, i)
         if h in (0, 5, 11):
             vn = v[0, h].float().cpu().numpy()
             on = o[0, h].float().cpu().numpy()
             # tile 6 and 244 are partial (4 of 8 W columns); 122 is interior
-            tiles = sorted(set(rng.choice(nT, 4, replace=False).tolist()) | {0, 6, 122, nT - 1})
-            ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+            tiles = unambiguous(sorted(set(rng.choice(nT, 4, replace=False).tolist()) | {0, 6, 122, nT - 1}),
+                                margins)
+            ref = attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=tiles)
             for i in tiles:
                 err = np.abs(on[mem[i]] - ref[mem[i]]).max()
                 assert err <= ATOL, (h, i, err)
@@ -248,11 +249,10 @@ def test_maximum_sizes(name):
     nT = len(mem)
     assert plan.info.n_tiles[0] == nT
     got = csr_rows(row_ptr, col, 0, plan.info.max_tiles, nT)
-    for i in range(nT):
-        if margins[i] > 1e-9:
-            assert got[i] == rows[i], i
-    tiles = list(range(nT)) if nT <= 2 else sorted(set(range(0, nT, 37)) | {nT - 1})
-    ref = attention.block_sparse_attention(qn, kn, vn, mem, got, query_tiles=tiles)
+    for i in unambiguous(range(nT), margins):
+        assert got[i] == rows[i], i
+    tiles = unambiguous(list(range(nT)) if nT <= 2 else sorted(set(range(0, nT, 37)) | {nT - 1}), margins)
+    ref = attention.block_sparse_attention(qn, kn, vn, mem, rows, query_tiles=tiles)
     on = o[0, 0].float().cpu().numpy()
     for i in tiles:
         err = np.abs(on[mem[i]] - ref[mem[i]]).max()
