@@ -178,11 +178,3 @@ def select_rows(S, ntiles, window=None, win_mode="truncate", k=0, p=0.0, sink=0)
         rows.append(sorted(keep))
         margins.append(margin)
     return rows, margins
-
-
-def to_csr(rows):
-    """List of sorted rows -> (row_ptr int32, col_idx int32)."""
-    row_ptr = np.zeros(len(rows) + 1, dtype=np.int32)
-    row_ptr[1:] = np.cumsum([len(r) for r in rows])
-    col_idx = np.array([j for r in rows for j in r], dtype=np.int32)
-    return row_ptr, col_idx

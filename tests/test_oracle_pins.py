@@ -439,3 +439,47 @@ def test_fine_attention_dense_when_all_kept():
     g = fine.groups(70, 32)
     got = attention.fine_attention(q, k, v, g, [np.arange(70)] * len(g))
     assert np.allclose(got, attention.attention_dense(q, k, v), rtol=1e-12, atol=1e-13)
+
+
+def test_tile_sics_equals_bruteforce_per_tile():
+    """Per-tile SICS against explicit pairwise cosines over every token pair
+    of each (ragged) tile."""
+    grid, tile = (3, 5, 7), (2, 3, 4)
+    x = _bf16((3 * 5 * 7, 16), 31).astype(np.float64)
+    mem = geometry.tile_members(grid, tile)
+    got = sics.tile_sics(x, mem)
+    for i, m in enumerate(mem):
+        want = 0.0
+        for a, b in itertools.combinations(m, 2):
+            want += float(x[a] @ x[b]) / (np.linalg.norm(x[a]) * np.linalg.norm(x[b]))
+        assert math.isclose(got[i], want, rel_tol=1e-10, abs_tol=1e-10), (i, got[i], want)
+
+
+def test_mean_pair_cosine_special_cases():
+    """Parallel tokens give 1 per pair, orthonormal tokens 0; one-token tiles
+    are left out of the mean."""
+    grid, tile = (1, 4, 6), (1, 2, 3)
+    mem = geometry.tile_members(grid, tile)
+    par = np.tile(np.arange(1.0, 9.0), (24, 1))
+    assert math.isclose(sics.mean_pair_cosine(par, mem), 1.0, rel_tol=1e-12)
+    orth = np.zeros((24, 24))
+    orth[np.arange(24), np.arange(24)] = 1.0
+    assert abs(sics.mean_pair_cosine(orth, mem)) < 1e-15
+    mem1 = [[0], [1, 2]]                      # a one-token tile and a pair of opposite tokens
+    x = np.array([[1.0, 0.0], [0.0, 1.0], [0.0, -1.0]])
+    assert math.isclose(sics.mean_pair_cosine(x, mem1), -1.0, rel_tol=1e-12)
+
+
+def test_token_tile_id_bruteforce():
+    """Tile id of every token of a ragged grid by explicit coordinate loops."""
+    grid, tile = (5, 7, 9), (2, 3, 4)
+    nt = [-(-g // t) for g, t in zip(grid, tile)]
+    want = [((t // tile[0]) * nt[1] + h // tile[1]) * nt[2] + w // tile[2]
+            for t in range(grid[0]) for h in range(grid[1]) for w in range(grid[2])]
+    assert geometry.token_tile_id(grid, tile).tolist() == want
+
+
+def test_default_scale():
+    assert select.default_scale(64) == 0.125
+    assert select.default_scale(128) == 1.0 / math.sqrt(128.0)
+    assert math.isclose(select.default_scale(128) ** 2 * 128, 1.0, rel_tol=1e-15)
