@@ -151,6 +151,9 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   if (pr->d != 64 && pr->d != 128) return fail(VSA_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", pr->d);
   long N = (long)pr->grid[0] * pr->grid[1] * pr->grid[2];
   if (N > (1L << 30)) return fail(VSA_ERR_UNSUPPORTED, "too many tokens");
+  // several launches put B*H in the second grid dimension
+  const long BH = (long)pr->B * pr->H;
+  if (BH > 65535) return fail(VSA_ERR_UNSUPPORTED, "B*H = %ld exceeds 65535", BH);
   uint32_t f = po->flags;
   const uint32_t known = VSA_DENSE | VSA_WINDOW | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP |
                          VSA_SICS_SELECT | VSA_FINE | VSA_PROFILE_SELECT;
@@ -204,6 +207,8 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       return fail(VSA_ERR_INVALID_ARG, "fine_keep must be in (0, 1]");
     g.fine_M = M;
     g.fine_G = (int)ceil_div(N, M);
+    if (BH * g.fine_G > 0x7fffffffL)  // the fine-mask passes index (head, group) pairs in 32 bits
+      return fail(VSA_ERR_UNSUPPORTED, "B*H*groups = %ld exceeds 2^31 - 1", BH * g.fine_G);
     double total = (double)g.fine_G * (double)N;
     g.fine_keep = frac_count(po->fine_keep, (long)total);
     g.fine_cap = std::min((long)total, g.fine_keep + N);
@@ -248,6 +253,10 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       g.max_tiles = std::max(g.max_tiles, b.n_tiles);
       g.tok_cap = std::max(g.tok_cap, (long)b.n_tiles * b.slots);
     }
+    // the attention launch has one workgroup per (head, tile, group of at
+    // most 12 slabs of 32 query rows): at most 11 groups per tile
+    if (BH * g.max_tiles * 11 > 0x7fffffffL)
+      return fail(VSA_ERR_UNSUPPORTED, "B*H*tiles = %ld is too large for one launch", BH * g.max_tiles);
     if (f & VSA_TOPP) {
       if (!(po->topp > 0.0 && po->topp <= 1.0))
         return fail(VSA_ERR_INVALID_ARG, "topp must be in (0, 1]");
@@ -340,7 +349,6 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   }
 
   // Workspace layout.
-  const long BH = (long)g.B * g.H;
   size_t sz[VSA_WS_NREGIONS] = {0};
   if (!(f & VSA_FINE)) {
     size_t tm = (size_t)BH * g.tok_cap * g.d * 2;

@@ -145,6 +145,12 @@ def test_plan_errors():
     assert _err(ok, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), compute=2)) == vsa._lib.VSA_ERR_INVALID_ARG
     assert _err(ok, vsa.make_policy(vsa.VSA_FINE, fine_group=64, fine_keep=0.1,
                                     compute=vsa.VSA_COMPUTE_FP8)) == vsa._lib.VSA_ERR_UNSUPPORTED
+    # launch-size limits: B*H in the second grid dimension; one attention workgroup per
+    # (head, tile, slab group) in a 1-D launch; (head, group) pairs of the fine path in 32 bits
+    assert _err(vsa.make_problem(256, 256, 64, (4, 8, 8), (2, 4, 4)), win) == vsa._lib.VSA_ERR_UNSUPPORTED
+    assert _err(vsa.make_problem(60, 1000, 64, (16, 16, 16), (1, 1, 1)), win) == vsa._lib.VSA_ERR_UNSUPPORTED
+    assert _err(vsa.make_problem(1, 1024, 64, (1024, 1024, 1024), (1, 1, 1)),
+                vsa.make_policy(vsa.VSA_FINE, fine_group=16, fine_keep=0.1)) == vsa._lib.VSA_ERR_UNSUPPORTED
     with pytest.raises(vsa.VsaError):
         vsa.vsa_plan(None, win) if False else _lib._check(vsa.lib().vsa_plan(None, None, None))
 
