@@ -73,6 +73,53 @@ void axis_range(int c, int r, int n, int mode, int* lo, int* hi) {
   }
 }
 
+// Kept key tiles of query tile i under the static part of the policy
+// (window box, or every tile under VSA_DENSE / no window, plus the sink),
+// marked in `keep` (n_tiles flags).
+void static_row(const Geo& g, const BlkGeo& b, int i, std::vector<char>& keep) {
+  std::fill(keep.begin(), keep.end(), 0);
+  int lo[3] = {0, 0, 0}, hi[3] = {b.nt[0] - 1, b.nt[1] - 1, b.nt[2] - 1};
+  if (!(g.flags & VSA_DENSE) && (g.flags & VSA_WINDOW)) {
+    const int c3[3] = {i / (b.nt[1] * b.nt[2]), (i / b.nt[2]) % b.nt[1], i % b.nt[2]};
+    for (int a = 0; a < 3; ++a) axis_range(c3[a], (g.win[a] - 1) / 2, b.nt[a], g.win_mode, &lo[a], &hi[a]);
+  }
+  if ((g.flags & (VSA_DENSE | VSA_WINDOW)) != 0)
+    for (int t = lo[0]; t <= hi[0]; ++t)
+      for (int h = lo[1]; h <= hi[1]; ++h)
+        for (int w = lo[2]; w <= hi[2]; ++w) keep[(t * b.nt[1] + h) * b.nt[2] + w] = 1;
+  for (int j = 0; j < std::min(g.sink, b.n_tiles); ++j) keep[j] = 1;
+}
+
+// Whether the attention launch pairs adjacent query tiles (2p, 2p+1) of a
+// blocking in one workgroup that streams the union of their kept lists.
+// Only groups of 4 to 6 waves (tiles of 97..192 slots) are paired, giving
+// 8- to 12-wave workgroups with a 4-stage ring.  Top-P rows keep most tiles
+// and neighbours' rows nearly coincide; Top-K rows of neighbours overlap far
+// less, so they are not paired; static masks are paired when the pairs'
+// lists overlap enough that at least 70% of the staged chunks serve both
+// tiles' waves.
+int pair_tiles(const Geo& g, const BlkGeo& b) {
+  const int slabs = b.slots / 32;
+  if (slabs < 4 || slabs > 6) return 0;
+  if (g.flags & VSA_TOPP) return 1;
+  if (g.flags & (VSA_TOPK | VSA_TOPK_FRAC)) return 0;
+  std::vector<char> ka(b.n_tiles), kb(b.n_tiles);
+  double used = 0.0, staged = 0.0;
+  for (int i = 0; i < b.n_tiles; i += 2) {
+    static_row(g, b, i, ka);
+    if (i + 1 < b.n_tiles) static_row(g, b, i + 1, kb); else std::fill(kb.begin(), kb.end(), 0);
+    long na = 0, nb = 0, nu = 0;
+    for (int j = 0; j < b.n_tiles; ++j) {
+      na += ka[j];
+      nb += kb[j];
+      nu += (ka[j] | kb[j]);
+    }
+    used += (double)(na + nb);
+    staged += 2.0 * (double)nu;
+  }
+  return staged > 0.0 && used >= 0.7 * staged ? 1 : 0;
+}
+
 // Valid tokens of tile (it, ih, iw) of a blocking.
 long tile_valid(const Geo& g, const BlkGeo& b, int it, int ih, int iw) {
   long et = std::min(b.tile[0], g.grid[0] - it * b.tile[0]);
@@ -273,6 +320,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
         win_cells *= po->win[a];
       }
     }
+    for (int c = 0; c < g.nb; ++c) g.blk[c].pair = pair_tiles(g, g.blk[c]);
     p->dynamic = (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP | VSA_SICS_SELECT | VSA_PROFILE_SELECT)) != 0;
     if ((f & (VSA_DENSE | VSA_TOPP)) || (f & (VSA_SICS_SELECT | VSA_PROFILE_SELECT))) {
       g.row_cap = g.max_tiles;
@@ -485,6 +533,7 @@ int vsa_plan_get_info(const vsa_plan_t* p, vsa_plan_info* info) {
     info->n_tiles[c] = g.blk[c].n_tiles;
     info->slots[c] = g.blk[c].slots;
     info->topk[c] = g.blk[c].topk;
+    info->pair[c] = g.blk[c].pair;
   }
   info->max_tiles = g.max_tiles;
   info->row_cap = g.row_cap;

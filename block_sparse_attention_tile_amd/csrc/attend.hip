@@ -98,9 +98,13 @@ __device__ __forceinline__ long token_of(const Geo& g, const BlkGeo& b, const Ti
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // The kept-tile list in LDS holds, per entry, the key tile j in the low
-// kTileBits bits and its valid key count above them (tiles are limited to
-// 4096 of at most 4096 tokens), so the chunk iterators never divide.
+// kTileBits bits, its valid key count in the next kTileBits bits (tiles are
+// limited to 4096 of at most 4096 tokens, so the chunk iterators never
+// divide), and above them which of the workgroup's query tiles keep it
+// (bit 0: the first, bit 1: the second of a pair).
 constexpr int kTileBits = 13;
+constexpr int kFlagShift = 2 * kTileBits;
+__device__ __forceinline__ int entry_nv(int x) { return (x >> kTileBits) & ((1 << kTileBits) - 1); }
 
 // Iterator over the 64-key chunks of a query tile's kept key tiles.
 struct ChunkIter {
@@ -108,16 +112,19 @@ struct ChunkIter {
   int j;    // key tile
   int off;  // first slot of the chunk inside tile j
   int nv;   // valid keys of tile j
+  int fl;   // query tiles of the workgroup that keep tile j
   __device__ __forceinline__ void load(const int* cols) {
     const int x = __builtin_amdgcn_readfirstlane(cols[e]);  // uniform: keep the iterator scalar
     j = x & ((1 << kTileBits) - 1);
-    nv = x >> kTileBits;
+    nv = entry_nv(x);
+    fl = x >> kFlagShift;
   }
   __device__ __forceinline__ void start(const int* cols, int L) {
     e = 0;
     off = 0;
     j = 0;
     nv = 0;
+    fl = 0;
     if (L > 0) load(cols);
   }
   __device__ __forceinline__ void next(const int* cols, int L) {
@@ -216,7 +223,10 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 // so two small workgroups can share a CU.
 constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
-template <class C, int NW, int STAGES>
+// TPW query tiles per workgroup (1, or 2 for a pair of adjacent tiles whose
+// waves share the staged chunks of the union of their kept lists); NW / TPW
+// waves per query tile.
+template <class C, int NW, int STAGES, int TPW>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     Geo g, int blocking, const typename C::T* __restrict__ qt, const typename C::T* __restrict__ kt,
     const typename C::T* __restrict__ vt, const int* __restrict__ row_len,
@@ -228,19 +238,22 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   extern __shared__ __align__(16) unsigned char lds_bytes[];
   T* const lds = reinterpret_cast<T*>(lds_bytes);
   using Loader = ChunkLoader<C, NW>;
+  constexpr int WPT = NW / TPW;  // waves per query tile
+  static_assert(TPW == 1 || TPW == 2, "one tile or a pair per workgroup");
 
   // XCD-major mapping of workgroups to work items.
+  const int units = (g.max_tiles + TPW - 1) / TPW;  // tiles (or pairs) per head
   const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
   const int item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
   if (item >= n_items) return;
   const int sb = item % nsb;
-  const int i = (item / nsb) % g.max_tiles;
-  const long bh = item / (nsb * g.max_tiles);
+  const int i0 = ((item / nsb) % units) * TPW;  // first query tile of the workgroup
+  const long bh = item / (nsb * units);
   if (cand_of(g, cand, bh) != blocking) return;
   const BlkGeo b = pick_blk(g, blocking);
-  if (i >= b.n_tiles) return;
+  if (i0 >= b.n_tiles) return;
   const int slots = b.slots;
-  const int q0 = sb * NW * 32;
+  const int q0 = sb * WPT * 32;
   if (q0 >= slots) return;
 
   const int tid = threadIdx.x;
@@ -248,19 +261,53 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   const int wave = tid >> 6;
   const int col = lane & 31;  // query column inside the wave's 32 rows
   const int hi = lane >> 5;   // wave half
-  const int qrow = q0 + wave * 32;  // first query row of this wave
-  const bool active = qrow < slots;
+  const int sub = wave / WPT;          // which query tile of the workgroup this wave serves
+  const int i = i0 + sub;              // that query tile
+  const int qrow = q0 + (wave - sub * WPT) * 32;  // first query row of this wave
+  const bool active = i < b.n_tiles && qrow < slots;
   const long head_tm = bh * g.tok_cap * D;
 
   // kept-tile list -> LDS (after the K/V stages)
   int* cols = reinterpret_cast<int*>(lds + STAGES * Stage::STAGE);
-  // (row length and tile indices clamped: a selection that was never
+  // (row lengths and tile indices clamped: a selection that was never
   // written still keeps every access in bounds)
-  const int L = min(max(row_len[bh * g.max_tiles + i], 0), g.row_cap);
-  const int* gcols = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
-  for (int e = tid; e < L; e += NW * 64) {
-    const int j = min(max(gcols[e], 0), b.n_tiles - 1);
-    cols[e] = (tile_nvalid(g, b, j) << kTileBits) | j;
+  int L;
+  if constexpr (TPW == 1) {
+    L = min(max(row_len[bh * g.max_tiles + i0], 0), g.row_cap);
+    const int* gcols = col_idx + (bh * g.max_tiles + i0) * (long)g.row_cap;
+    for (int e = tid; e < L; e += NW * 64) {
+      const int j = min(max(gcols[e], 0), b.n_tiles - 1);
+      cols[e] = (1 << kFlagShift) | (tile_nvalid(g, b, j) << kTileBits) | j;
+    }
+  } else {
+    // both tiles' lists, then their ascending union with per-tile flags
+    // (each tile then meets its own kept tiles in its own list's order)
+    int* la = cols + 2 * g.row_cap;
+    int* lb = la + g.row_cap;
+    int* nu = lb + g.row_cap;
+    const bool has_b = i0 + 1 < b.n_tiles;
+    const int na = min(max(row_len[bh * g.max_tiles + i0], 0), g.row_cap);
+    const int nb = has_b ? min(max(row_len[bh * g.max_tiles + i0 + 1], 0), g.row_cap) : 0;
+    const int* ga = col_idx + (bh * g.max_tiles + i0) * (long)g.row_cap;
+    const int* gb = ga + g.row_cap;
+    for (int e = tid; e < na; e += NW * 64) la[e] = min(max(ga[e], 0), b.n_tiles - 1);
+    for (int e = tid; e < nb; e += NW * 64) lb[e] = min(max(gb[e], 0), b.n_tiles - 1);
+    __syncthreads();
+    if (tid == 0) {
+      int ia = 0, ib = 0, n = 0;
+      while (ia < na || ib < nb) {  // every pass consumes at least one entry
+        const int ja = ia < na ? la[ia] : 0x7fffffff;
+        const int jb = ib < nb ? lb[ib] : 0x7fffffff;
+        const int j = min(ja, jb);
+        const int fl = (ja == j ? 1 : 0) | (jb == j ? 2 : 0);
+        ia += ja == j;
+        ib += jb == j;
+        cols[n++] = (fl << kFlagShift) | (tile_nvalid(g, b, j) << kTileBits) | j;
+      }
+      *nu = n;
+    }
+    __syncthreads();
+    L = *nu;
   }
 
   typename C::WS ws;
@@ -282,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 
   // total chunks of the row (each wave sums the list on its own)
   int total = 0;
-  for (int e = lane; e < L; e += 64) total += ((cols[e] >> kTileBits) + kKC - 1) / kKC;
+  for (int e = lane; e < L; e += 64) total += (entry_nv(cols[e]) + kKC - 1) / kKC;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) total += __shfl_xor(total, m);
   total = __builtin_amdgcn_readfirstlane(total);
@@ -323,7 +370,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     for (int u = 0; u < CPB; ++u) {
       if (c + u < total) {
         const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
-        if (active) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+        if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
         cur.next(cols, L);
       }
     }
@@ -344,8 +391,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 // several implicit instantiations sharing a wave count, taking a kernel's
 // host-side address for hipFuncSetAttribute has left some host stubs
 // undefined in the shared library.)
-#define VSA_ATTEND_INST(C, NW, ST)                                                             \
-  template __global__ void attend_kernel<C, NW, ST>(Geo, int, const typename C::T*,           \
+#define VSA_ATTEND_INST(C, NW, ST) VSA_ATTEND_INST_T(C, NW, ST, 1)
+#define VSA_ATTEND_INST_T(C, NW, ST, TPW)                                                      \
+  template __global__ void attend_kernel<C, NW, ST, TPW>(Geo, int, const typename C::T*,      \
                                                     const typename C::T*, const typename C::T*, \
                                                     const int*, const int*, const int*,        \
                                                     const int*, uint16_t*, int, int);
@@ -353,32 +401,43 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   VSA_ATTEND_INST(C, 1, 2) VSA_ATTEND_INST(C, 2, 2) VSA_ATTEND_INST(C, 3, 2)    \
   VSA_ATTEND_INST(C, 4, 2) VSA_ATTEND_INST(C, 5, 2) VSA_ATTEND_INST(C, 6, 2)    \
   VSA_ATTEND_INST(C, 7, 2) VSA_ATTEND_INST(C, 8, 2) VSA_ATTEND_INST(C, 7, 4) VSA_ATTEND_INST(C, 8, 4) VSA_ATTEND_INST(C, 9, 4)    \
-  VSA_ATTEND_INST(C, 10, 4) VSA_ATTEND_INST(C, 11, 4) VSA_ATTEND_INST(C, 12, 4)
+  VSA_ATTEND_INST(C, 10, 4) VSA_ATTEND_INST(C, 11, 4) VSA_ATTEND_INST(C, 12, 4)        \
+  VSA_ATTEND_INST_T(C, 8, 4, 2) VSA_ATTEND_INST_T(C, 10, 4, 2) VSA_ATTEND_INST_T(C, 12, 4, 2)
 VSA_ATTEND_INST_C(Bf16Core<128>)
 VSA_ATTEND_INST_C(Bf16Core<64>)
 VSA_ATTEND_INST_C(F8Core<128>)
 VSA_ATTEND_INST_C(F8Core<64>)
 #undef VSA_ATTEND_INST_C
+#undef VSA_ATTEND_INST_T
 #undef VSA_ATTEND_INST
 
-template <class C, int NW, int STAGES>
+// Dynamic LDS of a launch: the K/V ring, then the kept list (TPW = 1) or the
+// union (up to twice a row), both tiles' lists and the union's length.
+template <class C, int STAGES, int TPW>
+size_t attend_shmem(const Geo& g) {
+  const size_t list_ints = TPW == 1 ? (size_t)g.row_cap : 4 * (size_t)g.row_cap + 1;
+  return (size_t)STAGES * C::L::STAGE * sizeof(typename C::T) + list_ints * 4;
+}
+
+template <class C, int NW, int STAGES, int TPW = 1>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
   using T = typename C::T;
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
-  const int nsb = (slabs + NW - 1) / NW;
-  const long items = (long)g.B * g.H * g.max_tiles * nsb;
+  const int nsb = (slabs + NW / TPW - 1) / (NW / TPW);
+  const long units = (g.max_tiles + TPW - 1) / TPW;
+  const long items = (long)g.B * g.H * units * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
-  const size_t shmem = (size_t)STAGES * C::L::STAGE * sizeof(T) + (size_t)g.row_cap * 4;
+  const size_t shmem = attend_shmem<C, STAGES, TPW>(g);
   static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
   if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<C, NW, STAGES>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+  hipLaunchKernelGGL((attend_kernel<C, NW, STAGES, TPW>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, reinterpret_cast<const T*>(w.qt), reinterpret_cast<const T*>(w.kt),
                      reinterpret_cast<const T*>(w.vt), w.row_len, w.col_idx, cand, w.f8_exp, o, nsb,
                      (int)items);
@@ -398,6 +457,15 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
   const int slabs = g.blk[blocking].slots / 32;
   const int groups = (slabs + kMaxWaves - 1) / kMaxWaves;
   const int nw = (slabs + groups - 1) / groups;
+  // a pair of adjacent query tiles per workgroup (the plan decides; 4 to 6
+  // waves per tile), when the ring and the lists fit in the CU's LDS
+  if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2>(g) <= 160 * 1024) {
+    switch (nw) {
+      case 4: return launch_one<C, 8, 4, 2>(g, w, blocking, cand, o, s);
+      case 5: return launch_one<C, 10, 4, 2>(g, w, blocking, cand, o, s);
+      default: return launch_one<C, 12, 4, 2>(g, w, blocking, cand, o, s);
+    }
+  }
   switch (nw) {
     case 1: return launch_one<C, 1, 2>(g, w, blocking, cand, o, s);
     case 2: return launch_one<C, 2, 2>(g, w, blocking, cand, o, s);

@@ -16,6 +16,7 @@ struct BlkGeo {
   int n_tiles;   // nt[0]*nt[1]*nt[2]
   int slots;     // tokens per tile rounded up to a multiple of 32
   int topk;      // resolved K for this blocking (0 = off)
+  int pair;      // attention: two adjacent query tiles per workgroup (their kept lists overlap)
 };
 
 // Everything a kernel needs to know about the problem; passed by value.

@@ -176,6 +176,11 @@ typedef struct vsa_plan_info {
   int64_t fine_keep_count;        /* kept (group, key) pairs per head target */
   int64_t fine_cap;               /* capacity of the kept-key list per head */
   double scale;                   /* resolved softmax scale */
+  int32_t pair[VSA_MAX_CAND];     /* 1: the attention of this blocking runs two adjacent
+                                     query tiles per workgroup over the union of their
+                                     kept lists (tiles of 4 to 6 slabs; Top-P masks, or
+                                     static masks whose neighbours' lists mostly
+                                     coincide) */
 } vsa_plan_info;
 
 /* Workspace regions, for inspection by tests (see vsa_workspace_region). */

@@ -222,3 +222,21 @@ def test_profile_errors_and_sizes():
     assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_SSE)[1] == 2 * runs * 2 * 4
     segs = min(-(-1024 // (2 * 1)), 4 * 8, 16)  # groups = B*H*ceil(runs/4) = 2; lines = 32
     assert vsa.vsa_workspace_region(h, _lib.VSA_WS_PROF_PART)[1] == 2 * runs * segs * 32 * (64 + 2) * 4
+
+
+def test_attention_pairs_query_tiles_where_lists_overlap():
+    """Plan-time choice of two query tiles per attention workgroup: tiles of 4 to 6 slabs
+    under Top-P, or under a static mask whose neighbours' lists mostly coincide; never for
+    Top-K, a 1x1x1 window or larger tiles."""
+    from synth import CONFIGS, Workload
+    from block_sparse_attention_tile_amd.workload import plan_structs
+
+    def pair(wl):
+        p = vsa.Plan(*plan_structs(wl))
+        return list(p.info.pair)[:p.info.n_blockings]
+    assert pair(CONFIGS["wan480"]) == [1]
+    assert pair(Workload("w", 1, 2, 128, (3, 18, 20), (3, 6, 8), window=(3, 3, 3))) == [1]
+    assert pair(Workload("w", 1, 2, 128, (6, 12, 40), (3, 6, 8), window=(1, 1, 1))) == [0]
+    assert pair(Workload("k", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3)) == [0]
+    assert pair(CONFIGS["hunyuan"]) == [0]
+    assert pair(CONFIGS["wan14b"]) == [0, 0, 0]

@@ -45,6 +45,9 @@ SMALL = {
     "eight_slab": Workload("eight_slab", 1, 2, 128, (4, 16, 32), (1, 16, 16), window=(3, 1, 1), topk=2),
     # seven slabs (224-token tiles), ragged on every axis, Top-P, d=64
     "seven_slab_ragged": Workload("seven_slab_ragged", 1, 2, 64, (5, 9, 30), (2, 8, 14), topp=0.9),
+    # static window over 144-token tiles: query tiles run in pairs (union of their kept
+    # lists); 9 tiles, so the last pair has one tile, and the last W tile is half full
+    "pair_window_odd": Workload("pair_window_odd", 1, 2, 128, (3, 18, 20), (3, 6, 8), window=(3, 3, 3)),
 }
 
 
