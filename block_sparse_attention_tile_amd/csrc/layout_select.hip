@@ -321,7 +321,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
   // are exact in any order too.
   double* red = reinterpret_cast<double*>(smem);  // [kLayoutThreads][8]
   float* redf = reinterpret_cast<float*>(smem);   // [kLayoutThreads][8]
-  const long dst_off = (bh * g.max_tiles + i) * D;
+  // Q summaries [head][tile][d]; K summaries channel-major [head][d][tile],
+  // so that the selection's per-key-tile dot products read them coalesced
+  const long q_off = (bh * g.max_tiles + i) * D;
+  const long k_off = bh * D * (long)g.max_tiles + i;
   for (int which = 0; which < 2; ++which) {
     if (which == 1 && extrema) break;  // K gets its extrema below instead of its mean
 #pragma unroll
@@ -331,8 +334,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
       const int pp = tid / 8, xx = tid % 8;
       double s = 0.0;
       for (int r = 0; r < RPP; ++r) s += red[(r * P + pp) * 8 + xx];
-      float* dst = which ? pooled_k : pooled_q;
-      dst[dst_off + tid] = (float)(s / (double)t.nvalid);
+      const float m = (float)(s / (double)t.nvalid);
+      if (which)
+        pooled_k[k_off + (long)tid * g.max_tiles] = m;
+      else
+        pooled_q[q_off + tid] = m;
     }
     __syncthreads();
   }
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
         const float v = redf[(r * P + pp) * 8 + xx];
         m = which ? fminf(m, v) : fmaxf(m, v);
       }
-      (which ? pooled_kmin : pooled_k)[dst_off + tid] = m;
+      (which ? pooled_kmin : pooled_k)[k_off + (long)tid * g.max_tiles] = m;
     }
     __syncthreads();
   }
@@ -379,6 +385,7 @@ __global__ __launch_bounds__(kLayoutThreads) void untile_kernel(Geo g, const uin
 // Selection: one workgroup per (head, query tile).
 
 constexpr int kSelThreads = 256;
+constexpr int kSelBatch = 16;  // channels loaded per batch (d is a multiple of 16)
 constexpr int kMaxTiles = 4096;
 
 __device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
@@ -443,16 +450,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
     while (m < n) m <<= 1;
     for (int j = tid; j < m; j += kSelThreads) {
       if (j < n) {
-        const float* kr = pooled_k + (bh * g.max_tiles + j) * D;
+        // channel x of key tile j at [x][j]: consecutive lanes read consecutive words
+        const float* kr = pooled_k + bh * D * (long)g.max_tiles + j;
         double acc = 0.0;
         // Fixed left-to-right order; each fp32 x fp32 product is exact in
         // fp64, so a fused multiply-add rounds exactly like mul-then-add.
         if (g.summ == VSA_SUMM_MINMAX) {
-          const float* kn = pooled_kmin + (bh * g.max_tiles + j) * D;
-          for (int x = 0; x < D; ++x)
-            acc += fmax((double)qbar[x] * (double)kr[x], (double)qbar[x] * (double)kn[x]);
+          const float* kn = pooled_kmin + bh * D * (long)g.max_tiles + j;
+          for (int x0 = 0; x0 < D; x0 += kSelBatch) {
+            float a[kSelBatch], c[kSelBatch];  // a batch of loads in flight, then the sums in order
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) {
+              a[u] = kr[(long)(x0 + u) * g.max_tiles];
+              c[u] = kn[(long)(x0 + u) * g.max_tiles];
+            }
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u)
+              acc += fmax((double)qbar[x0 + u] * (double)a[u], (double)qbar[x0 + u] * (double)c[u]);
+          }
         } else {
-          for (int x = 0; x < D; ++x) acc = fma((double)qbar[x], (double)kr[x], acc);
+          for (int x0 = 0; x0 < D; x0 += kSelBatch) {
+            float a[kSelBatch];
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) a[u] = kr[(long)(x0 + u) * g.max_tiles];
+#pragma unroll
+            for (int u = 0; u < kSelBatch; ++u) acc = fma((double)qbar[x0 + u], (double)a[u], acc);
+          }
         }
         sc[j] = acc * g.scale;
         sid[j] = j;
@@ -484,15 +507,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
       }
     }
     for (int r = tid; r < K; r += kSelThreads) keep[sid[r]] = 1;
-    if (topp && tid == 0) {
+    if (topp) {
+      // softmax weights of the sorted row, every thread its share of the
+      // exponentials (in place: the scores are not needed afterwards); then
+      // one thread sums them and walks the cumulative mass in sorted order
       const double mx = sc[0];
-      double z = 0.0;
-      for (int r = 0; r < n; ++r) z += exp(sc[r] - mx);
-      double cum = 0.0;
-      for (int r = 0; r < n; ++r) {
-        keep[sid[r]] = 1;
-        cum += exp(sc[r] - mx) / z;
-        if (cum >= g.topp) break;
+      __syncthreads();  // every thread has read sc[0]
+      for (int r = tid; r < n; r += kSelThreads) sc[r] = exp(sc[r] - mx);
+      __syncthreads();
+      if (tid == 0) {
+        double z = 0.0;
+        for (int r = 0; r < n; ++r) z += sc[r];
+        double cum = 0.0;
+        for (int r = 0; r < n; ++r) {
+          keep[sid[r]] = 1;
+          cum += sc[r] / z;
+          if (cum >= g.topp) break;
+        }
       }
     }
   }

@@ -188,7 +188,7 @@ typedef struct vsa_plan_info {
 #define VSA_WS_KT          1  /* bf16 [B*H][tiles*slots][d] tile-major K */
 #define VSA_WS_VT          2  /* bf16 [B*H][tiles][d][slots] tile-major V, transposed per tile */
 #define VSA_WS_POOLED_Q    3  /* fp32 [B*H][max_tiles][d] mean of Q */
-#define VSA_WS_POOLED_K    4  /* fp32 [B*H][max_tiles][d] mean (or, VSA_SUMM_MAX / MINMAX, maximum) of K */
+#define VSA_WS_POOLED_K    4  /* fp32 [B*H][d][max_tiles] (channel-major) mean (or, VSA_SUMM_MAX / MINMAX, maximum) of K */
 #define VSA_WS_ROW_LEN     5  /* int32 [B*H][max_tiles] kept tiles per row */
 #define VSA_WS_COL_IDX     6  /* int32 [B*H][max_tiles][row_cap] ascending */
 #define VSA_WS_CAND        7  /* int32 [B*H] chosen blocking */
@@ -202,7 +202,7 @@ typedef struct vsa_plan_info {
 #define VSA_WS_FINE_PTR   15  /* int32 [B*H][G+1] start of each group's keys */
 #define VSA_WS_FINE_SCORE 16  /* fp64 [B*H][G][N] group-key scores */
 #define VSA_WS_SCRATCH    17  /* internal */
-#define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][max_tiles][d] per-channel K minimum (VSA_SUMM_MINMAX) */
+#define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][d][max_tiles] (channel-major) per-channel K minimum (VSA_SUMM_MINMAX) */
 #define VSA_WS_F8_EXP     19  /* int32 [B*H][3] exponents e_q, e_k, e_v (VSA_COMPUTE_FP8) */
 #define VSA_WS_F8_AMAX    20  /* uint32 [B*H][3][parts] partial max |x| as bf16 bits (VSA_COMPUTE_FP8) */
 #define VSA_WS_PROF_SSE   21  /* fp32 [B*H][runs][n_blockings] squared-error sums (VSA_PROFILE_SELECT) */

@@ -102,9 +102,10 @@ def test_pooled_means_bit_exact(name):
     mem = geometry.tile_members(wl.grid, wl.tile)
     nT = len(mem)
     pq = plan.region(_lib.VSA_WS_POOLED_Q, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
-    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
+    # K summaries are channel-major [head][d][tile]
+    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.B * wl.H, wl.d, nT).transpose(1, 2).cpu().numpy()
     if wl.summarizer == "minmax":
-        pkn = plan.region(_lib.VSA_WS_POOLED_KMIN, torch.float32).view(wl.B * wl.H, nT, wl.d).cpu().numpy()
+        pkn = plan.region(_lib.VSA_WS_POOLED_KMIN, torch.float32).view(wl.B * wl.H, wl.d, nT).transpose(1, 2).cpu().numpy()
     qn, kn = q.float().cpu().numpy(), k.float().cpu().numpy()
     for b in range(wl.B):
         for h in range(wl.H):
@@ -199,7 +200,7 @@ def test_wan480_full_size_sampled():
     mem = geometry.tile_members(wl.grid, wl.tile)
     assert nT == len(mem) == 245
     pq = plan.region(_lib.VSA_WS_POOLED_Q, torch.float32).view(wl.H, nT, wl.d).cpu().numpy()
-    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.H, nT, wl.d).cpu().numpy()
+    pk = plan.region(_lib.VSA_WS_POOLED_K, torch.float32).view(wl.H, wl.d, nT).transpose(1, 2).cpu().numpy()
     rng = np.random.default_rng(1)
     near_cut = 0
     for h in range(wl.H):
