@@ -145,10 +145,15 @@ __global__ __launch_bounds__(256, 2) void fine_score_kernel(Geo g, const uint16_
   for (int t = 0; t < kScoreKeys; ++t)
 #pragma unroll
     for (int x = 0; x < kScoreGroups; ++x) acc[t][x] = 0.0;
-  for (int p8 = 0; p8 < D / 8; ++p8) {
-    u32x4 w4[kScoreKeys];
+  // the next 8 channels of every key are loaded while these 8 are summed
+  u32x4 w4[kScoreKeys], nx[kScoreKeys];
 #pragma unroll
-    for (int t = 0; t < kScoreKeys; ++t) w4[t] = *reinterpret_cast<const u32x4*>(kr[t] + p8 * 8);
+  for (int t = 0; t < kScoreKeys; ++t) w4[t] = *reinterpret_cast<const u32x4*>(kr[t]);
+  for (int p8 = 0; p8 < D / 8; ++p8) {
+    if (p8 + 1 < D / 8) {
+#pragma unroll
+      for (int t = 0; t < kScoreKeys; ++t) nx[t] = *reinterpret_cast<const u32x4*>(kr[t] + (p8 + 1) * 8);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = p8 * 8 + e;
@@ -168,6 +173,8 @@ __global__ __launch_bounds__(256, 2) void fine_score_kernel(Geo g, const uint16_
         }
       }
     }
+#pragma unroll
+    for (int t = 0; t < kScoreKeys; ++t) w4[t] = nx[t];
   }
   unsigned long long kmin = ~0ull, kmax = 0ull;
 #pragma unroll
