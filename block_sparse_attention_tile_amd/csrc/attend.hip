@@ -104,6 +104,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (bit 0: the first, bit 1: the second of a pair).
 constexpr int kTileBits = 13;
 constexpr int kFlagShift = 2 * kTileBits;
+constexpr int kUnitNvShift = kTileBits + 8;  // unit-table entries: valid keys of the unit
 __device__ __forceinline__ int entry_nv(int x) { return (x >> kTileBits) & ((1 << kTileBits) - 1); }
 
 // Iterator over the 64-key chunks of a query tile's kept key tiles.
@@ -135,6 +136,12 @@ struct ChunkIter {
     }
   }
   __device__ __forceinline__ int keys() const { return min(kKC, nv - off); }
+};
+
+// Unit mode: element offsets of the first key of a chunk's four 16-key
+// units in the head's K (k0..k3) and V^T (v0..v3).
+struct UnitBases {
+  int k0, k1, k2, k3, v0, v1, v2, v3;
 };
 
 // Direct global->LDS loads of one chunk (K: 64 keys x D, V^T: D x 64 keys).
@@ -209,7 +216,66 @@ struct ChunkLoader {
                                        (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))), 16, 0, 0);
     }
   }
+
+  // Unit mode (bf16): a chunk is four 16-key units, each from its own key
+  // tile.  Piece x of this lane belongs to unit unit_of[x] (K: key row / 16;
+  // V^T: 16-byte key column / 2) and sits at off_full[x] inside it.
+  int unit_of[PER];
+
+  __device__ __forceinline__ void init_units(int w, int ln, int slots) {
+    static_assert(E == 8, "16-key units of 16-byte V^T columns need two-byte elements");
+    wave = __builtin_amdgcn_readfirstlane(w);
+    lane = ln;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int ins = ins_of(wave, x);
+      const int u = ins * 64 + lane;
+      if (ins < KI) {
+        const int key = L::key_of_row(u / (L::KC16 + 1));
+        const int c = min(u % (L::KC16 + 1), L::KC16 - 1);
+        unit_of[x] = key >> 4;
+        off_full[x] = (key & 15) * D + c * E;
+      } else {
+        const int v = u - KU;
+        const int d = v / (L::VC16 + 1);
+        const int c = min(v % (L::VC16 + 1), L::VC16 - 1);
+        unit_of[x] = c >> 1;
+        off_full[x] = d * slots + (c & 1) * E;
+      }
+    }
+  }
+
+  // u.k[t] / u.v[t]: element offsets of unit t's first key in the head's K
+  // and V^T (wave-uniform; named scalars, so the per-lane pick stays two
+  // levels of selects instead of an indexed private array).
+  __device__ __forceinline__ static int pick(int u, int b0, int b1, int b2, int b3) {
+    const int lo = (u & 1) ? b1 : b0;
+    const int hi = (u & 1) ? b3 : b2;
+    return (u & 2) ? hi : lo;
+  }
+  __device__ __forceinline__ void issue_units(T* stage, const T* __restrict__ kt_head,
+                                              const T* __restrict__ vt_head, const UnitBases& ub) const {
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      if (wave + x * NW >= NI) break;  // wave-uniform
+      const int ins = ins_of(wave, x);
+      const T* src = ins < KI ? kt_head + pick(unit_of[x], ub.k0, ub.k1, ub.k2, ub.k3)
+                              : vt_head + pick(unit_of[x], ub.v0, ub.v1, ub.v2, ub.v3);
+      __builtin_amdgcn_global_load_lds(src + off_full[x], (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))),
+                                       16, 0, 0);
+    }
+  }
 };
+
+// K and V^T element offsets of the first key of a unit-table entry.
+template <int D>
+__device__ __forceinline__ void unit_bases(int entry, int slots, int& kb, int& vb) {
+  const int x = __builtin_amdgcn_readfirstlane(entry);
+  const int j = x & ((1 << kTileBits) - 1);
+  const int uo = 16 * ((x >> kTileBits) & 255);
+  kb = (j * slots + uo) * D;
+  vb = j * D * slots + uo;
+}
 
 // All of this wave's outstanding loads have landed, then barrier: after it
 // every wave's pieces of the chunks issued so far are visible in LDS, and
@@ -225,8 +291,11 @@ constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
 // TPW query tiles per workgroup (1, or 2 for a pair of adjacent tiles whose
 // waves share the staged chunks of the union of their kept lists); NW / TPW
-// waves per query tile.
-template <class C, int NW, int STAGES, int TPW>
+// waves per query tile.  UN (bf16 pairs): the kept keys are cut into 16-key
+// units (a tile of nv keys gives ceil(nv / 16)), taken four per chunk in list
+// order, so a tile's short tail shares its chunk with the next tile's keys
+// instead of occupying a 32-key chunk of its own.
+template <class C, int NW, int STAGES, int TPW, bool UN>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     Geo g, int blocking, const typename C::T* __restrict__ qt, const typename C::T* __restrict__ kt,
     const typename C::T* __restrict__ vt, const int* __restrict__ row_len,
@@ -240,6 +309,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   using Loader = ChunkLoader<C, NW>;
   constexpr int WPT = NW / TPW;  // waves per query tile
   static_assert(TPW == 1 || TPW == 2, "one tile or a pair per workgroup");
+  static_assert(!UN || (TPW == 2 && !C::kF8), "16-key units: bf16 pairs");
 
   // XCD-major mapping of workgroups to work items.
   const int units = (g.max_tiles + TPW - 1) / TPW;  // tiles (or pairs) per head
@@ -305,9 +375,38 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
         cols[n++] = (fl << kFlagShift) | (tile_nvalid(g, b, j) << kTileBits) | j;
       }
       *nu = n;
+      if constexpr (UN) {
+        // first unit of each union entry (la, lb are free now), total units
+        // (ascending tile order: a 32-key block that mixes tiles kept by one
+        // query tile each keeps both halves of the workgroup busy)
+        int U = 0;
+        for (int e = 0; e < n; ++e) {
+          la[e] = U;
+          U += (entry_nv(cols[e]) + 15) >> 4;
+        }
+        nu[1] = U;
+      }
     }
     __syncthreads();
     L = *nu;
+  }
+  // Unit table: entry t holds tile (bits 0..12), unit within the tile
+  // (13..20), valid keys of the unit (21..25) and the pair flags (26, 27);
+  // padded to whole chunks with empty units of a kept tile.
+  int* const utab = cols + ((4 * g.row_cap + 2 + 3) & ~3);
+  int n_units = 0;
+  if constexpr (UN) {
+    const int* ust = cols + 2 * g.row_cap;
+    for (int e = tid; e < L; e += NW * 64) {
+      const int x = cols[e];
+      const int j = x & ((1 << kTileBits) - 1);
+      const int nv = entry_nv(x);
+      const int hd = j | ((x >> kFlagShift) << kFlagShift);
+      int* dst = utab + ust[e];
+      for (int t = 0; 16 * t < nv; ++t) dst[t] = hd | (t << kTileBits) | (min(16, nv - 16 * t) << kUnitNvShift);
+    }
+    n_units = cols[4 * g.row_cap + 1];  // nu[1]
+    if (tid < ((4 - (n_units & 3)) & 3)) utab[n_units + tid] = cols[0] & ((1 << kTileBits) - 1);
   }
 
   typename C::WS ws;
@@ -324,21 +423,25 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     oscale = __builtin_amdgcn_ldexpf(1.f, -ev);
   }
   Loader ldr;
-  ldr.init(wave, lane, slots);
-  __syncthreads();  // cols visible
+  if constexpr (UN)
+    ldr.init_units(wave, lane, slots);
+  else
+    ldr.init(wave, lane, slots);
+  __syncthreads();  // cols (and the unit table) visible
 
   // total chunks of the row (each wave sums the list on its own)
   int total = 0;
-  for (int e = lane; e < L; e += 64) total += (entry_nv(cols[e]) + kKC - 1) / kKC;
+  if constexpr (UN) {
+    total = (n_units + 3) >> 2;
+  } else {
+    for (int e = lane; e < L; e += 64) total += (entry_nv(cols[e]) + kKC - 1) / kKC;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) total += __shfl_xor(total, m);
+    for (int m = 32; m >= 1; m >>= 1) total += __shfl_xor(total, m);
+  }
   total = __builtin_amdgcn_readfirstlane(total);
 
   const T* kt_head = kt + head_tm;
   const T* vt_head = vt + head_tm;
-  ChunkIter ld_it, cur;
-  ld_it.start(cols, L);
-  cur = ld_it;
   // The ring holds STAGES chunks in two halves of CPB = STAGES/2 chunks.  The
   // prologue loads the first half; each iteration waits for the half it is
   // about to multiply (everything issued so far), refills the other half
@@ -346,32 +449,72 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   // per CPB chunks, CPB chunks always in flight.
   constexpr int CPB = STAGES / 2;
   static_assert(STAGES >= 2 && STAGES % 2 == 0, "stages come in pairs");
+  if constexpr (UN) {
+    const int wsub = __builtin_amdgcn_readfirstlane(sub);
+    auto issue_chunk = [&](int st, int nc) {
+      UnitBases ub;
+      unit_bases<D>(utab[4 * nc + 0], slots, ub.k0, ub.v0);
+      unit_bases<D>(utab[4 * nc + 1], slots, ub.k1, ub.v1);
+      unit_bases<D>(utab[4 * nc + 2], slots, ub.k2, ub.v2);
+      unit_bases<D>(utab[4 * nc + 3], slots, ub.k3, ub.v3);
+      ldr.issue_units(lds + st * Stage::STAGE, kt_head, vt_head, ub);
+    };
 #pragma unroll
-  for (int s = 0; s < CPB; ++s) {
-    if (s < total) {
-      ldr.issue(lds + s * Stage::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
-                vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-      ld_it.next(cols, L);
+    for (int s = 0; s < CPB; ++s)
+      if (s < total) issue_chunk(s, s);
+    for (int c = 0; c < total; c += CPB) {
+      wait_loads_and_barrier();
+#pragma unroll
+      for (int u = 0; u < CPB; ++u) {
+        const int nc = c + CPB + u;
+        if (nc < total) issue_chunk(nc % STAGES, nc);
+      }
+#pragma unroll
+      for (int u = 0; u < CPB; ++u) {
+        if (c + u < total) {
+          // valid keys of each unit for this wave's query tile
+          int n[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int x = __builtin_amdgcn_readfirstlane(utab[4 * (c + u) + t]);
+            n[t] = ((x >> (kFlagShift + wsub)) & 1) ? (x >> kUnitNvShift) & 31 : 0;
+          }
+          const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
+          if (active && n[0] + n[1] + n[2] + n[3] > 0) ws.chunk_units(lk, lk + Stage::KE, n, c2, col, hi);
+        }
+      }
     }
-  }
-  for (int c = 0; c < total; c += CPB) {
-    wait_loads_and_barrier();
+  } else {
+    ChunkIter ld_it, cur;
+    ld_it.start(cols, L);
+    cur = ld_it;
 #pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int nc = c + CPB + u;
-      if (nc < total) {
-        ldr.issue(lds + (nc % STAGES) * Stage::STAGE,
-                  kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+    for (int s = 0; s < CPB; ++s) {
+      if (s < total) {
+        ldr.issue(lds + s * Stage::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                   vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
         ld_it.next(cols, L);
       }
     }
+    for (int c = 0; c < total; c += CPB) {
+      wait_loads_and_barrier();
 #pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      if (c + u < total) {
-        const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
-        if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
-        cur.next(cols, L);
+      for (int u = 0; u < CPB; ++u) {
+        const int nc = c + CPB + u;
+        if (nc < total) {
+          ldr.issue(lds + (nc % STAGES) * Stage::STAGE,
+                    kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+                    vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
+          ld_it.next(cols, L);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CPB; ++u) {
+        if (c + u < total) {
+          const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
+          if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+          cur.next(cols, L);
+        }
       }
     }
   }
@@ -391,9 +534,10 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
 // several implicit instantiations sharing a wave count, taking a kernel's
 // host-side address for hipFuncSetAttribute has left some host stubs
 // undefined in the shared library.)
-#define VSA_ATTEND_INST(C, NW, ST) VSA_ATTEND_INST_T(C, NW, ST, 1)
-#define VSA_ATTEND_INST_T(C, NW, ST, TPW)                                                      \
-  template __global__ void attend_kernel<C, NW, ST, TPW>(Geo, int, const typename C::T*,      \
+#define VSA_ATTEND_INST(C, NW, ST) VSA_ATTEND_INST_U(C, NW, ST, 1, false)
+#define VSA_ATTEND_INST_T(C, NW, ST, TPW) VSA_ATTEND_INST_U(C, NW, ST, TPW, false)
+#define VSA_ATTEND_INST_U(C, NW, ST, TPW, UN)                                                  \
+  template __global__ void attend_kernel<C, NW, ST, TPW, UN>(Geo, int, const typename C::T*,  \
                                                     const typename C::T*, const typename C::T*, \
                                                     const int*, const int*, const int*,        \
                                                     const int*, uint16_t*, int, int);
@@ -403,23 +547,36 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   VSA_ATTEND_INST(C, 7, 2) VSA_ATTEND_INST(C, 8, 2) VSA_ATTEND_INST(C, 7, 4) VSA_ATTEND_INST(C, 8, 4) VSA_ATTEND_INST(C, 9, 4)    \
   VSA_ATTEND_INST(C, 10, 4) VSA_ATTEND_INST(C, 11, 4) VSA_ATTEND_INST(C, 12, 4)        \
   VSA_ATTEND_INST_T(C, 8, 4, 2) VSA_ATTEND_INST_T(C, 10, 4, 2) VSA_ATTEND_INST_T(C, 12, 4, 2)
+#define VSA_ATTEND_INST_UN(C) \
+  VSA_ATTEND_INST_U(C, 8, 4, 2, true) VSA_ATTEND_INST_U(C, 10, 4, 2, true) VSA_ATTEND_INST_U(C, 12, 4, 2, true)
 VSA_ATTEND_INST_C(Bf16Core<128>)
 VSA_ATTEND_INST_C(Bf16Core<64>)
 VSA_ATTEND_INST_C(F8Core<128>)
 VSA_ATTEND_INST_C(F8Core<64>)
+VSA_ATTEND_INST_UN(Bf16Core<128>)
+VSA_ATTEND_INST_UN(Bf16Core<64>)
+#undef VSA_ATTEND_INST_UN
 #undef VSA_ATTEND_INST_C
+#undef VSA_ATTEND_INST_U
 #undef VSA_ATTEND_INST_T
 #undef VSA_ATTEND_INST
 
 // Dynamic LDS of a launch: the K/V ring, then the kept list (TPW = 1) or the
-// union (up to twice a row), both tiles' lists and the union's length.
-template <class C, int STAGES, int TPW>
-size_t attend_shmem(const Geo& g) {
-  const size_t list_ints = TPW == 1 ? (size_t)g.row_cap : 4 * (size_t)g.row_cap + 1;
+// union (up to twice a row), both tiles' lists and the union's length; in
+// unit mode also the total units and the unit table (the union's entries
+// times the units of a full tile, padded to whole chunks).
+template <class C, int STAGES, int TPW, bool UN = false>
+size_t attend_shmem(const Geo& g, int blocking) {
+  size_t list_ints = TPW == 1 ? (size_t)g.row_cap : 4 * (size_t)g.row_cap + 1;
+  if (UN) {
+    const size_t entries = std::min<size_t>(2 * (size_t)g.row_cap, (size_t)g.blk[blocking].n_tiles);
+    list_ints = ((4 * (size_t)g.row_cap + 2 + 3) & ~(size_t)3) +
+                ((entries * (g.blk[blocking].slots / 16) + 3) & ~(size_t)3);
+  }
   return (size_t)STAGES * C::L::STAGE * sizeof(typename C::T) + list_ints * 4;
 }
 
-template <class C, int NW, int STAGES, int TPW = 1>
+template <class C, int NW, int STAGES, int TPW = 1, bool UN = false>
 hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
                       hipStream_t s) {
   using T = typename C::T;
@@ -429,15 +586,15 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
   const long units = (g.max_tiles + TPW - 1) / TPW;
   const long items = (long)g.B * g.H * units * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
-  const size_t shmem = attend_shmem<C, STAGES, TPW>(g);
+  const size_t shmem = attend_shmem<C, STAGES, TPW, UN>(g, blocking);
   static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
   if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW, UN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
     attr_bytes = shmem;
   }
-  hipLaunchKernelGGL((attend_kernel<C, NW, STAGES, TPW>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
+  hipLaunchKernelGGL((attend_kernel<C, NW, STAGES, TPW, UN>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, reinterpret_cast<const T*>(w.qt), reinterpret_cast<const T*>(w.kt),
                      reinterpret_cast<const T*>(w.vt), w.row_len, w.col_idx, cand, w.f8_exp, o, nsb,
                      (int)items);
@@ -459,7 +616,19 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
   const int nw = (slabs + groups - 1) / groups;
   // a pair of adjacent query tiles per workgroup (the plan decides; 4 to 6
   // waves per tile), when the ring and the lists fit in the CU's LDS
-  if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2>(g) <= 160 * 1024) {
+  if constexpr (!C::kF8) {
+    // bf16 pairs cut the kept keys into 16-key units when the table fits
+    // (and the head's element offsets fit in 32 bits)
+    if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2, true>(g, blocking) <= 160 * 1024 &&
+        g.tok_cap * C::D <= 0x7fffffffL) {
+      switch (nw) {
+        case 4: return launch_one<C, 8, 4, 2, true>(g, w, blocking, cand, o, s);
+        case 5: return launch_one<C, 10, 4, 2, true>(g, w, blocking, cand, o, s);
+        default: return launch_one<C, 12, 4, 2, true>(g, w, blocking, cand, o, s);
+      }
+    }
+  }
+  if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2>(g, blocking) <= 160 * 1024) {
     switch (nw) {
       case 4: return launch_one<C, 8, 4, 2>(g, w, blocking, cand, o, s);
       case 5: return launch_one<C, 10, 4, 2>(g, w, blocking, cand, o, s);

@@ -128,6 +128,18 @@ struct WaveState {
       if (16 * (r >> 3) + (r & 7) >= thr) s[r] = -INFINITY;
   }
 
+  // Per 16-key half h of a block (registers 8h .. 8h+7): keys at or past
+  // n_h (0..16) of the half get -inf.
+  __device__ __forceinline__ static void mask_halves(f32x16& s, int n0, int n1, int hi) {
+    int t0 = n0 - 8 * hi, t1 = n1 - 8 * hi;
+    asm volatile("" : "+v"(t0), "+v"(t1));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r >= t0) s[r] = -INFINITY;
+      if (r >= t1) s[8 + r] = -INFINITY;
+    }
+  }
+
   // Probabilities of a block against the current offset, as the bf16 B
   // operands of the two 16-key steps.
   __device__ __forceinline__ void probs(const f32x16& s, float c2, bf16x8 pb[2]) const {
@@ -201,6 +213,23 @@ struct WaveState {
       bf16x8 p1[2];
       softmax(s1, c2, p1);
       pv(lvt, 1, col, hi, p1);
+    }
+  }
+
+  // One staged chunk of four 16-key units with n[u] (0..16) valid keys each
+  // (wave-uniform).  A block whose two units hold no valid key is skipped;
+  // any other has a valid key in every query row, so its softmax is finite.
+  __device__ __forceinline__ void chunk_units(const uint16_t* lk, const uint16_t* lvt, const int n[4],
+                                              float c2, int col, int hi) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int na = n[2 * kb], nb = n[2 * kb + 1];
+      if (na + nb == 0) continue;
+      f32x16 s = scores(lk, kb, col, hi);
+      if (na < 16 || nb < 16) mask_halves(s, na, nb, hi);
+      bf16x8 p[2];
+      softmax(s, c2, p);
+      pv(lvt, kb, col, hi, p);
     }
   }
 

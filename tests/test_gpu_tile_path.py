@@ -48,6 +48,12 @@ SMALL = {
     # static window over 144-token tiles: query tiles run in pairs (union of their kept
     # lists); 9 tiles, so the last pair has one tile, and the last W tile is half full
     "pair_window_odd": Workload("pair_window_odd", 1, 2, 128, (3, 18, 20), (3, 6, 8), window=(3, 3, 3)),
+    # paired 105-token tiles (4 slabs): 16-key units with 9 valid keys end every full
+    # tile, 45-token edge tiles end with 13; Top-P + window
+    "pair_units_105": Workload("pair_units_105", 1, 2, 128, (6, 10, 17), (3, 5, 7), window=(3, 3, 3),
+                               topp=0.9),
+    # paired 180-token tiles (6 slabs), d=64, 120-token edge tiles, Top-P only
+    "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 15), topp=0.8),
 }
 
 
