@@ -135,6 +135,24 @@ long tile_valid_id(const Geo& g, const BlkGeo& b, int i) {
   return tile_valid(g, b, it, ih, iw);
 }
 
+// Whether the bf16 attention of a paired blocking stages the kept keys in
+// 16-key units (four per 64-key chunk, across tile boundaries) instead of
+// per-tile 64-key chunks with a 32-key tail chunk: when units cut the chunk
+// iterations over all tiles by at least 5% (tile sizes that are not
+// multiples of 64, or ragged edge tiles).  E4M3 always stages whole chunks.
+// (One-tile workgroups stay with whole chunks: units measured no faster
+// there, on 112-, 208- and 480-key tiles.)
+int unit_tiles(const Geo& g, const BlkGeo& b) {
+  if (g.f8 || !b.pair) return 0;
+  long units = 0, chunks = 0;
+  for (int i = 0; i < b.n_tiles; ++i) {
+    const long nv = tile_valid_id(g, b, i);
+    units += (nv + 15) / 16;
+    chunks += (nv + 63) / 64;
+  }
+  return 20 * units < 19 * 4 * chunks ? 1 : 0;
+}
+
 int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
 Ws resolve(const vsa_plan_t* p, void* ws) {
@@ -320,7 +338,10 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
         win_cells *= po->win[a];
       }
     }
-    for (int c = 0; c < g.nb; ++c) g.blk[c].pair = pair_tiles(g, g.blk[c]);
+    for (int c = 0; c < g.nb; ++c) {
+      g.blk[c].pair = pair_tiles(g, g.blk[c]);
+      g.blk[c].units = unit_tiles(g, g.blk[c]);
+    }
     p->dynamic = (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP | VSA_SICS_SELECT | VSA_PROFILE_SELECT)) != 0;
     if ((f & (VSA_DENSE | VSA_TOPP)) || (f & (VSA_SICS_SELECT | VSA_PROFILE_SELECT))) {
       g.row_cap = g.max_tiles;
@@ -534,6 +555,7 @@ int vsa_plan_get_info(const vsa_plan_t* p, vsa_plan_info* info) {
     info->slots[c] = g.blk[c].slots;
     info->topk[c] = g.blk[c].topk;
     info->pair[c] = g.blk[c].pair;
+    info->units[c] = g.blk[c].units;
   }
   info->max_tiles = g.max_tiles;
   info->row_cap = g.row_cap;

@@ -291,7 +291,8 @@ constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
 // TPW query tiles per workgroup (1, or 2 for a pair of adjacent tiles whose
 // waves share the staged chunks of the union of their kept lists); NW / TPW
-// waves per query tile.  UN (bf16 pairs): the kept keys are cut into 16-key
+// waves per query tile.  UN (bf16 pairs whose tile sizes leave short tails):
+// the kept keys are cut into 16-key
 // units (a tile of nv keys gives ceil(nv / 16)), taken four per chunk in list
 // order, so a tile's short tail shares its chunk with the next tile's keys
 // instead of occupying a 32-key chunk of its own.
@@ -617,10 +618,10 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
   // a pair of adjacent query tiles per workgroup (the plan decides; 4 to 6
   // waves per tile), when the ring and the lists fit in the CU's LDS
   if constexpr (!C::kF8) {
-    // bf16 pairs cut the kept keys into 16-key units when the table fits
-    // (and the head's element offsets fit in 32 bits)
-    if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2, true>(g, blocking) <= 160 * 1024 &&
-        g.tok_cap * C::D <= 0x7fffffffL) {
+    // bf16 pairs cut the kept keys into 16-key units where the plan chose
+    // them, the table fits and the head's element offsets fit in 32 bits
+    if (g.blk[blocking].pair && g.blk[blocking].units && nw >= 4 && nw <= 6 &&
+        attend_shmem<C, 4, 2, true>(g, blocking) <= 160 * 1024 && g.tok_cap * C::D <= 0x7fffffffL) {
       switch (nw) {
         case 4: return launch_one<C, 8, 4, 2, true>(g, w, blocking, cand, o, s);
         case 5: return launch_one<C, 10, 4, 2, true>(g, w, blocking, cand, o, s);

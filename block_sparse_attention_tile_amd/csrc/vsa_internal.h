@@ -17,6 +17,7 @@ struct BlkGeo {
   int slots;     // tokens per tile rounded up to a multiple of 32
   int topk;      // resolved K for this blocking (0 = off)
   int pair;      // attention: two adjacent query tiles per workgroup (their kept lists overlap)
+  int units;     // attention (bf16 pairs): keys staged in 16-key units, four per 64-key chunk
 };
 
 // Everything a kernel needs to know about the problem; passed by value.

@@ -240,3 +240,24 @@ def test_attention_pairs_query_tiles_where_lists_overlap():
     assert pair(Workload("k", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3)) == [0]
     assert pair(CONFIGS["hunyuan"]) == [0]
     assert pair(CONFIGS["wan14b"]) == [0, 0, 0]
+
+
+def test_attention_units_where_tails_are_short():
+    """Plan-time choice of 16-key units (bf16 pairs): when they cut the chunk count over all
+    tiles by 5% or more, as for 144-token tiles (9 units vs 3 chunks) or 168-token ones (11
+    vs 12); not for 180-token tiles (12 units = 3 chunks), not for unpaired blockings, never
+    for E4M3."""
+    from synth import CONFIGS, Workload
+    from block_sparse_attention_tile_amd.workload import plan_structs
+
+    def units(wl):
+        p = vsa.Plan(*plan_structs(wl))
+        return list(p.info.units)[:p.info.n_blockings]
+    assert units(CONFIGS["wan480"]) == [1]
+    assert units(CONFIGS["wan480"].with_(compute="fp8")) == [0]
+    assert units(CONFIGS["hunyuan"]) == [0]
+    assert units(CONFIGS["wan14b"]) == [0, 0, 0]
+    assert units(CONFIGS["hunyuan_svg"]) == [0, 0]
+    assert units(CONFIGS["tiny"]) == [0]
+    assert units(Workload("u", 1, 2, 64, (4, 12, 40), (2, 6, 15), topp=0.8)) == [0]   # 180 = 12 units = 3 chunks
+    assert units(Workload("u", 1, 2, 64, (4, 12, 40), (2, 6, 14), topp=0.8)) == [1]   # 168: 11 units < 3 chunks

@@ -52,8 +52,11 @@ SMALL = {
     # tile, 45-token edge tiles end with 13; Top-P + window
     "pair_units_105": Workload("pair_units_105", 1, 2, 128, (6, 10, 17), (3, 5, 7), window=(3, 3, 3),
                                topp=0.9),
-    # paired 180-token tiles (6 slabs), d=64, 120-token edge tiles, Top-P only
-    "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 15), topp=0.8),
+    # paired 168-token tiles (6 slabs, 16-key units), d=64, 144-token edge tiles, Top-P only
+    "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 14), topp=0.8),
+    # 336-token tiles (eleven-wave workgroups, 4-stage ring, a 16-key tail chunk per tile),
+    # static window, ragged H
+    "eleven_slab_units": Workload("eleven_slab_units", 1, 2, 128, (12, 13, 24), (6, 7, 8), window=(3, 3, 3)),
 }
 
 
