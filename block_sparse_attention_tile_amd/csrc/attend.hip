@@ -197,12 +197,18 @@ struct ChunkLoader {
   // The source offset of piece x for a 32-key chunk: K rows past 31 and V^T
   // key columns past 31 are clamped to the last valid ones (derived from the
   // 64-key offset: K rows are D apart, the V^T column unit is recomputed).
+  // With six or more pieces per lane, holding these offsets across the
+  // loop beside the 64-key ones spills; they are recomputed per 32-key chunk
+  // instead (the empty asm keeps the compiler from hoisting them).
   __device__ __forceinline__ int off_half(int x) const {
     constexpr int HU = L::VC16 / 2;  // data units of 32 keys
+    int o = off_full[x];
+    int ln = lane;
+    if constexpr (PER >= 6) asm volatile("" : "+v"(o), "+v"(ln));
     const int ins = ins_of(wave, x);
-    if (ins < KI) return min(off_full[x], 31 * D + (off_full[x] & (D - 1)));
-    const int c = min((ins * 64 + lane - KU) % (L::VC16 + 1), L::VC16 - 1);
-    return off_full[x] - max(c - (HU - 1), 0) * E;
+    if (ins < KI) return min(o, 31 * D + (o & (D - 1)));
+    const int c = min((ins * 64 + ln - KU) % (L::VC16 + 1), L::VC16 - 1);
+    return o - max(c - (HU - 1), 0) * E;
   }
 
   __device__ __forceinline__ void issue(T* stage, const T* __restrict__ kbase,
