@@ -501,7 +501,12 @@ hipError_t launch_fine_attend_t(const Geo& g, const Ws& w, const uint16_t* q, co
 template <int D>
 hipError_t launch_fine_attend_d(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, uint16_t* o, hipStream_t s) {
-  switch ((g.fine_M + 31) / 32) {
+  int nw = (g.fine_M + 31) / 32;
+  // At d = 128 one wave would hold a whole gathered chunk in its registers
+  // and spill; a second wave (whose rows belong to the next group, so it
+  // only gathers) halves that.
+  if (D == 128 && nw < 2) nw = 2;
+  switch (nw) {
     case 1: return launch_fine_attend_t<D, 1>(g, w, q, k, v, o, s);
     case 2: return launch_fine_attend_t<D, 2>(g, w, q, k, v, o, s);
     case 3: return launch_fine_attend_t<D, 3>(g, w, q, k, v, o, s);

@@ -25,6 +25,9 @@ SMALL = {
     "fine_dense": Workload("fine_dense", 1, 1, 128, (2, 8, 12), (1, 1, 1), fine_group=64, fine_keep=1.0),
     # M = 128 (four waves per group)
     "fine_m128": Workload("fine_m128", 1, 2, 128, (4, 8, 16), (1, 1, 1), fine_group=128, fine_keep=0.2),
+    # 32-row groups at d = 128 (a second, gather-only wave per workgroup), ragged last group
+    "fine_m32_d128": Workload("fine_m32_d128", 1, 2, 128, (3, 6, 11), (1, 1, 1), fine_group=32,
+                              fine_keep=0.2),
 }
 
 
