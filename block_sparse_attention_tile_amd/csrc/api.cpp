@@ -274,6 +274,8 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     g.fine_G = (int)ceil_div(N, M);
     if (BH * g.fine_G > 0x7fffffffL)  // the fine-mask passes index (head, group) pairs in 32 bits
       return fail(VSA_ERR_UNSUPPORTED, "B*H*groups = %ld exceeds 2^31 - 1", BH * g.fine_G);
+    if ((long)g.fine_G * N > 0x7fffffffL)  // candidate scores keep their (group, key) position in 32 bits
+      return fail(VSA_ERR_UNSUPPORTED, "groups*N = %ld exceeds 2^31 - 1", (long)g.fine_G * N);
     double total = (double)g.fine_G * (double)N;
     g.fine_keep = frac_count(po->fine_keep, (long)total);
     g.fine_cap = std::min((long)total, g.fine_keep + N);

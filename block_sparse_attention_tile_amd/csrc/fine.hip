@@ -53,6 +53,7 @@ struct FineScratch {
   int* hist;                      // [BH][kBins]
   double* qbar64;                 // [BH][G][D]
   unsigned long long* cand;       // [BH][kCandCap]
+  int* cpos;                      // [BH][kCandCap] position g * N + j of each candidate
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -68,6 +69,8 @@ FineScratch carve(const Geo& g, unsigned char* base) {
   f.qbar64 = reinterpret_cast<double*>(base + off);
   off = align256(off + (size_t)BH * g.fine_G * g.d * sizeof(double));
   f.cand = reinterpret_cast<unsigned long long*>(base + off);
+  off = align256(off + (size_t)BH * kCandCap * sizeof(unsigned long long));
+  f.cpos = reinterpret_cast<int*>(base + off);
   return f;
 }
 
@@ -86,7 +89,7 @@ __device__ __forceinline__ int score_bin(double s, double lo, double inv_w) {
   return b < 0 ? 0 : (b >= kBins ? kBins - 1 : b);
 }
 
-__global__ __launch_bounds__(256) void fine_init_kernel(FineScratch f) {
+__global__ __launch_bounds__(256) void fine_init_kernel(Geo g, FineScratch f, int* __restrict__ count) {
   const long bh = blockIdx.x;
   if (threadIdx.x == 0) {
     FineHead h = {};
@@ -95,6 +98,7 @@ __global__ __launch_bounds__(256) void fine_init_kernel(FineScratch f) {
     f.head[bh] = h;
   }
   for (int b = threadIdx.x; b < kBins; b += 256) f.hist[bh * kBins + b] = 0;
+  for (int gi = threadIdx.x; gi < g.fine_G; gi += 256) count[bh * g.fine_G + gi] = 0;
 }
 
 // Group means of Q: exact fp64 sums of at most M bf16 values per channel.
@@ -241,25 +245,64 @@ __global__ __launch_bounds__(64) void fine_find_kernel(Geo g, FineScratch f) {
   f.head[bh].ncand = 0;
 }
 
+// Candidates of the threshold bin (order key and position), and per group
+// the scores of higher bins: those are all kept, since the binning is
+// monotone and tau lies in the threshold bin.  Each thread counts its run of
+// one group in a register and adds it when the group changes, into LDS for
+// the span's first kSpanGroups groups (every one, unless N < 64), else into
+// the global count.
+constexpr int kSpanGroups = 1024;
 __global__ __launch_bounds__(256) void fine_gather_kernel(Geo g, const double* __restrict__ score,
-                                                          FineScratch f) {
+                                                          FineScratch f, int* __restrict__ count) {
+  __shared__ int cnt[kSpanGroups];
   const long bh = blockIdx.y;
   const long total = (long)g.fine_G * g.N;
   const long s0 = (long)blockIdx.x * kSpan;
   if (s0 >= total) return;
+  for (int x = threadIdx.x; x < kSpanGroups; x += 256) cnt[x] = 0;
+  __syncthreads();
   const double lo = okey_value(f.head[bh].kmin), hi = okey_value(f.head[bh].kmax);
   const double inv_w = hi > lo ? (double)kBins / (hi - lo) : 0.0;
   const int bin = f.head[bh].bin;
   const double* s = score + bh * total;
+  int* const gcount = count + bh * g.fine_G;
   const long s1 = min(total, s0 + kSpan);
-  for (long e = s0 + threadIdx.x; e < s1; e += 256) {
+  const int g_first = (int)(s0 / g.N);
+  long e = s0 + threadIdx.x;
+  int gi = (int)(e / g.N);
+  long g_end = (long)(gi + 1) * g.N;
+  int run = 0;
+  auto flush = [&]() {
+    if (run == 0) return;
+    if (gi - g_first < kSpanGroups) atomicAdd(&cnt[gi - g_first], run);
+    else atomicAdd(&gcount[gi], run);
+    run = 0;
+  };
+  for (; e < s1; e += 256) {
+    while (e >= g_end) {
+      flush();
+      ++gi;
+      g_end += g.N;
+    }
     const double v = s[e];
-    if (score_bin(v, lo, inv_w) == bin) {
+    const int sb = score_bin(v, lo, inv_w);
+    if (sb > bin) {
+      ++run;
+    } else if (sb == bin) {
       const int slot = atomicAdd(&f.head[bh].ncand, 1);
-      if (slot < kCandCap) f.cand[bh * kCandCap + slot] = okey(v);
-      else f.head[bh].overflow = 1;
+      if (slot < kCandCap) {
+        f.cand[bh * kCandCap + slot] = okey(v);
+        f.cpos[bh * kCandCap + slot] = (int)e;
+      } else {
+        f.head[bh].overflow = 1;
+      }
     }
   }
+  flush();
+  __syncthreads();
+  const int n_local = (int)min((long)kSpanGroups, (s1 - 1) / g.N - g_first + 1);
+  for (int x = threadIdx.x; x < n_local; x += 256)
+    if (cnt[x]) atomicAdd(&gcount[g_first + x], cnt[x]);
 }
 
 // Exact K-th largest: MSB-first radix select, 8 bits per pass, over the
@@ -301,12 +344,31 @@ __global__ __launch_bounds__(1024) void fine_select_kernel(Geo g, FineScratch f,
   if (threadIdx.x == 0) tau[bh] = okey_value(prefix_s);
 }
 
+// Kept scores per group, the threshold bin's share: candidates at or above
+// tau (the same fp64 comparison as the emit pass), added to the higher bins'
+// counts of the gather pass.
+__global__ __launch_bounds__(256) void fine_cand_count_kernel(Geo g, FineScratch f,
+                                                              const double* __restrict__ tau,
+                                                              int* __restrict__ count) {
+  const long bh = blockIdx.y;
+  if (f.head[bh].overflow & 1) return;  // the full count below runs instead
+  const int n = min((long)f.head[bh].ncand, kCandCap);
+  const double t = tau[bh];
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < n; e += gridDim.x * 256)
+    if (okey_value(f.cand[bh * kCandCap + e]) >= t)
+      atomicAdd(&count[bh * g.fine_G + f.cpos[bh * kCandCap + e] / g.N], 1);
+}
+
+// Full count of one group's kept scores, only when the candidates
+// overflowed (tau then comes from a partial candidate set, and the counts
+// must still match the emit pass).
 __global__ __launch_bounds__(256) void fine_count_kernel(Geo g, const double* __restrict__ score,
                                                          const double* __restrict__ tau,
-                                                         int* __restrict__ count) {
+                                                         FineScratch f, int* __restrict__ count) {
   __shared__ int part[4];
   const int gi = blockIdx.x;
   const long bh = blockIdx.y;
+  if (!(f.head[bh].overflow & 1)) return;
   const double t = tau[bh];
   const double* s = score + (bh * g.fine_G + gi) * (long)g.N;
   int c = 0;
@@ -525,7 +587,8 @@ size_t fine_scratch_bytes(const Geo& g) {
   size_t off = align256(BH * sizeof(FineHead));
   off = align256(off + BH * kBins * sizeof(int));
   off = align256(off + (size_t)BH * g.fine_G * g.d * sizeof(double));
-  off += (size_t)BH * kCandCap * sizeof(unsigned long long);
+  off = align256(off + (size_t)BH * kCandCap * sizeof(unsigned long long));
+  off += (size_t)BH * kCandCap * sizeof(int);
   return off;
 }
 
@@ -534,7 +597,7 @@ hipError_t launch_fine_select(const Geo& g, const Ws& w, const uint16_t* q, cons
   const FineScratch f = carve(g, w.scratch);
   const unsigned BH = (unsigned)(g.B * g.H);
   hipError_t e;
-  hipLaunchKernelGGL(fine_init_kernel, dim3(BH), dim3(256), 0, s, f);
+  hipLaunchKernelGGL(fine_init_kernel, dim3(BH), dim3(256), 0, s, g, f, w.fine_count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.d == 128)
     hipLaunchKernelGGL(fine_qbar_kernel<128>, dim3(g.fine_G, BH), dim3(128), 0, s, g, q, w.fine_qbar, f);
@@ -552,9 +615,10 @@ hipError_t launch_fine_select(const Geo& g, const Ws& w, const uint16_t* q, cons
   dim3 hg((unsigned)((total + kSpan - 1) / kSpan), BH);
   hipLaunchKernelGGL(fine_hist_kernel, hg, dim3(256), 0, s, g, score, f);
   hipLaunchKernelGGL(fine_find_kernel, dim3(BH), dim3(64), 0, s, g, f);
-  hipLaunchKernelGGL(fine_gather_kernel, hg, dim3(256), 0, s, g, score, f);
+  hipLaunchKernelGGL(fine_gather_kernel, hg, dim3(256), 0, s, g, score, f, w.fine_count);
   hipLaunchKernelGGL(fine_select_kernel, dim3(BH), dim3(1024), 0, s, g, f, w.fine_tau);
-  hipLaunchKernelGGL(fine_count_kernel, dim3(g.fine_G, BH), dim3(256), 0, s, g, score, w.fine_tau,
+  hipLaunchKernelGGL(fine_cand_count_kernel, dim3(64, BH), dim3(256), 0, s, g, f, w.fine_tau, w.fine_count);
+  hipLaunchKernelGGL(fine_count_kernel, dim3(g.fine_G, BH), dim3(256), 0, s, g, score, w.fine_tau, f,
                      w.fine_count);
   hipLaunchKernelGGL(fine_scan_kernel, dim3(BH), dim3(64), 0, s, g, w.fine_count, w.fine_ptr, f);
   hipLaunchKernelGGL(fine_emit_kernel, dim3(g.fine_G, BH), dim3(256), 0, s, g, score, w.fine_tau,

@@ -232,8 +232,9 @@ typedef struct vsa_plan_info {
  * (0,1], conflicting flags, an unknown compute mode; VSA_ERR_UNSUPPORTED
  * for d not in {64,128}, dtype other than bf16, VSA_COMPUTE_FP8 with
  * VSA_FINE, more than 4096 tiles, a tile larger than the grid, B*H above
- * 65535, or more workgroups than one launch holds (B*H*tiles*11 or
- * B*H*groups above 2^31 - 1). */
+ * 65535, more workgroups than one launch holds (B*H*tiles*11 or
+ * B*H*groups above 2^31 - 1), or, for VSA_FINE, groups*N above 2^31 - 1
+ * (the mask passes index a head's scores in 32 bits). */
 int vsa_plan(const vsa_problem* prob, const vsa_mask_policy* pol, vsa_plan_t** out);
 void vsa_plan_destroy(vsa_plan_t* plan);
 int vsa_plan_get_info(const vsa_plan_t* plan, vsa_plan_info* info);
