@@ -437,14 +437,16 @@ struct GatherLoader {
   // K pieces: piece-fastest (a key row is read by consecutive lanes).
   // V quads: 4 consecutive keys x 8 channels per thread, key quads fastest,
   // so that 16 lanes write one 128-byte run of a transposed LDS row.  Rows
-  // past the chunk re-read its last valid key.
+  // past the chunk re-read its last valid key.  The chunk's key indices come
+  // from an LDS copy (keys), so the row loads issue without waiting on a
+  // global load.
   int n_tok;  // tokens per head (key indices are clamped below it)
-  __device__ __forceinline__ int key_at(const int* __restrict__ keys, int r) const {
+  __device__ __forceinline__ int key_at(const int* keys, int r) const {
     return min(max(keys[r], 0), n_tok - 1);
   }
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
-                                       const int* __restrict__ keys, int nk) {
+                                       const int* keys, int nk) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
@@ -520,22 +522,33 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
 
   // One LDS stage: the next chunk's rows are gathered into registers while
   // the current one is multiplied, then written over it between two
-  // barriers (a small stage lets four workgroups share a CU).
+  // barriers (a small stage lets four workgroups share a CU).  Two 64-entry
+  // LDS buffers hold the key indices of the next chunks: chunk c's in buffer
+  // c % 2.  While chunk c is multiplied, wave 0 fetches the indices of chunk
+  // c + 2 into a register and writes them over chunk c's between the
+  // barriers.
+  int* const ibuf = reinterpret_cast<int*>(lds + Lds<D>::STAGE);
+  for (int x = tid; x < 2 * kKC; x += NW * 64) ibuf[x] = n > 0 ? keys[min(x, n - 1)] : 0;
+  __syncthreads();
   GatherLoader<D, NW> ld;
   ld.n_tok = g.N;
   if (n > 0) {
-    ld.load(k + head, v + head, keys, min(kKC, n));
+    ld.load(k + head, v + head, ibuf, min(kKC, n));
     ld.store(lds);
   }
   __syncthreads();
-  for (int e0 = 0; e0 < n; e0 += kKC) {
+  for (int e0 = 0, c = 0; e0 < n; e0 += kKC, ++c) {
     const int e1 = e0 + kKC;
     const bool has_next = e1 < n;
-    if (has_next) ld.load(k + head, v + head, keys + e1, min(kKC, n - e1));
+    const bool has_next2 = e1 + kKC < n;
+    int pf = 0;
+    if (has_next2 && tid < kKC) pf = keys[min(e1 + kKC + tid, n - 1)];
+    if (has_next) ld.load(k + head, v + head, ibuf + ((c + 1) & 1) * kKC, min(kKC, n - e1));
     if (active) ws.chunk(lds, lds + Lds<D>::KE, min(kKC, n - e0), c2, col, hi);
     if (has_next) {
       __syncthreads();
       ld.store(lds);
+      if (has_next2 && tid < kKC) ibuf[(c & 1) * kKC + tid] = pf;
       __syncthreads();
     }
   }
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
 template <int D, int NW>
 hipError_t launch_fine_attend_t(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, uint16_t* o, hipStream_t s) {
-  const size_t shmem = Lds<D>::STAGE * sizeof(uint16_t);
+  const size_t shmem = Lds<D>::STAGE * sizeof(uint16_t) + 2 * kKC * sizeof(int);  // stage, index buffers
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fine_attend_kernel<D, NW>),
