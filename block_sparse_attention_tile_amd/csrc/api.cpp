@@ -135,22 +135,23 @@ long tile_valid_id(const Geo& g, const BlkGeo& b, int i) {
   return tile_valid(g, b, it, ih, iw);
 }
 
-// Whether the bf16 attention of a paired blocking stages the kept keys in
-// 16-key units (four per 64-key chunk, across tile boundaries) instead of
-// per-tile 64-key chunks with a 32-key tail chunk: when units cut the chunk
-// iterations over all tiles by at least 5% (tile sizes that are not
-// multiples of 64, or ragged edge tiles).  E4M3 always stages whole chunks.
-// (One-tile workgroups stay with whole chunks: units measured no faster
+// Whether the attention of a paired blocking stages the kept keys in units
+// (16 keys for bf16, 32 for E4M3; 64 / unit size per 64-key chunk, across
+// tile boundaries) instead of per-tile 64-key chunks with a 32-key tail
+// chunk: when units cut the chunk iterations over all tiles by at least 5%
+// (tile sizes that are not multiples of 64, or ragged edge tiles).
+// (One-tile workgroups stay with whole chunks: bf16 units measured no faster
 // there, on 112-, 208- and 480-key tiles.)
 int unit_tiles(const Geo& g, const BlkGeo& b) {
-  if (g.f8 || !b.pair) return 0;
+  if (!b.pair) return 0;
+  const long ku = g.f8 ? 32 : 16;
   long units = 0, chunks = 0;
   for (int i = 0; i < b.n_tiles; ++i) {
     const long nv = tile_valid_id(g, b, i);
-    units += (nv + 15) / 16;
+    units += (nv + ku - 1) / ku;
     chunks += (nv + 63) / 64;
   }
-  return 20 * units < 19 * 4 * chunks ? 1 : 0;
+  return 20 * units < 19 * (64 / ku) * chunks ? 1 : 0;
 }
 
 int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }

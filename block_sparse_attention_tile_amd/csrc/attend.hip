@@ -104,7 +104,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (bit 0: the first, bit 1: the second of a pair).
 constexpr int kTileBits = 13;
 constexpr int kFlagShift = 2 * kTileBits;
-constexpr int kUnitNvShift = kTileBits + 8;  // unit-table entries: valid keys of the unit
+constexpr int kUnitNvShift = kTileBits + 8;  // unit-table entries: valid keys of the unit, minus 1
 __device__ __forceinline__ int entry_nv(int x) { return (x >> kTileBits) & ((1 << kTileBits) - 1); }
 
 // Iterator over the 64-key chunks of a query tile's kept key tiles.
@@ -223,13 +223,16 @@ struct ChunkLoader {
     }
   }
 
-  // Unit mode (bf16): a chunk is four 16-key units, each from its own key
-  // tile.  Piece x of this lane belongs to unit unit_of[x] (K: key row / 16;
-  // V^T: 16-byte key column / 2) and sits at off_full[x] inside it.
+  // Unit mode: a chunk is 64 / KU units of KU keys (16 for bf16, 32 for
+  // E4M3, whose V^T slot permutation stays inside 32-slot groups), each from
+  // its own key tile.  Piece x of this lane belongs to unit unit_of[x] (K:
+  // key row / KU; V^T: the 16-byte key column's first key / KU) and sits at
+  // off_full[x] inside it.
+  static constexpr int KU_ = C::kF8 ? 32 : 16;
   int unit_of[PER];
 
   __device__ __forceinline__ void init_units(int w, int ln, int slots) {
-    static_assert(E == 8, "16-key units of 16-byte V^T columns need two-byte elements");
+    static_assert(KU_ % E == 0, "a 16-byte V^T column lies inside one unit");
     wave = __builtin_amdgcn_readfirstlane(w);
     lane = ln;
 #pragma unroll
@@ -239,14 +242,14 @@ struct ChunkLoader {
       if (ins < KI) {
         const int key = L::key_of_row(u / (L::KC16 + 1));
         const int c = min(u % (L::KC16 + 1), L::KC16 - 1);
-        unit_of[x] = key >> 4;
-        off_full[x] = (key & 15) * D + c * E;
+        unit_of[x] = key / KU_;
+        off_full[x] = (key % KU_) * D + c * E;
       } else {
         const int v = u - KU;
         const int d = v / (L::VC16 + 1);
         const int c = min(v % (L::VC16 + 1), L::VC16 - 1);
-        unit_of[x] = c >> 1;
-        off_full[x] = d * slots + (c & 1) * E;
+        unit_of[x] = c * E / KU_;
+        off_full[x] = d * slots + (c * E) % KU_;
       }
     }
   }
@@ -274,11 +277,11 @@ struct ChunkLoader {
 };
 
 // K and V^T element offsets of the first key of a unit-table entry.
-template <int D>
+template <int D, int KU>
 __device__ __forceinline__ void unit_bases(int entry, int slots, int& kb, int& vb) {
   const int x = __builtin_amdgcn_readfirstlane(entry);
   const int j = x & ((1 << kTileBits) - 1);
-  const int uo = 16 * ((x >> kTileBits) & 255);
+  const int uo = KU * ((x >> kTileBits) & 255);
   kb = (j * slots + uo) * D;
   vb = j * D * slots + uo;
 }
@@ -297,11 +300,11 @@ constexpr int waves_per_simd(int nw) { return nw > 2 ? 3 : 2; }
 
 // TPW query tiles per workgroup (1, or 2 for a pair of adjacent tiles whose
 // waves share the staged chunks of the union of their kept lists); NW / TPW
-// waves per query tile.  UN (bf16 pairs whose tile sizes leave short tails):
-// the kept keys are cut into 16-key
-// units (a tile of nv keys gives ceil(nv / 16)), taken four per chunk in list
-// order, so a tile's short tail shares its chunk with the next tile's keys
-// instead of occupying a 32-key chunk of its own.
+// waves per query tile.  UN (pairs whose tile sizes leave short tails): the
+// kept keys are cut into 16-key (E4M3: 32-key)
+// units (a tile of nv keys gives ceil(nv / 16), or ceil(nv / 32)), taken
+// four (two) per chunk in list order, so a tile's short tail shares its chunk
+// with the next tile's keys instead of occupying a chunk of its own.
 template <class C, int NW, int STAGES, int TPW, bool UN>
 __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     Geo g, int blocking, const typename C::T* __restrict__ qt, const typename C::T* __restrict__ kt,
@@ -316,7 +319,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   using Loader = ChunkLoader<C, NW>;
   constexpr int WPT = NW / TPW;  // waves per query tile
   static_assert(TPW == 1 || TPW == 2, "one tile or a pair per workgroup");
-  static_assert(!UN || (TPW == 2 && !C::kF8), "16-key units: bf16 pairs");
+  static_assert(!UN || TPW == 2, "units: pairs");
+  constexpr int KU = C::kF8 ? 32 : 16;  // keys per unit (unit mode)
+  constexpr int UPC = kKC / KU;         // units per chunk
 
   // XCD-major mapping of workgroups to work items.
   const int units = (g.max_tiles + TPW - 1) / TPW;  // tiles (or pairs) per head
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
         int U = 0;
         for (int e = 0; e < n; ++e) {
           la[e] = U;
-          U += (entry_nv(cols[e]) + 15) >> 4;
+          U += (entry_nv(cols[e]) + KU - 1) / KU;
         }
         nu[1] = U;
       }
@@ -398,8 +403,9 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     L = *nu;
   }
   // Unit table: entry t holds tile (bits 0..12), unit within the tile
-  // (13..20), valid keys of the unit (21..25) and the pair flags (26, 27);
-  // padded to whole chunks with empty units of a kept tile.
+  // (13..20), valid keys of the unit minus one (21..25) and the pair flags
+  // (26, 27); padded to whole chunks with units of a kept tile that no query
+  // tile keeps (no flags).
   int* const utab = cols + ((4 * g.row_cap + 2 + 3) & ~3);
   int n_units = 0;
   if constexpr (UN) {
@@ -410,10 +416,10 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
       const int nv = entry_nv(x);
       const int hd = j | ((x >> kFlagShift) << kFlagShift);
       int* dst = utab + ust[e];
-      for (int t = 0; 16 * t < nv; ++t) dst[t] = hd | (t << kTileBits) | (min(16, nv - 16 * t) << kUnitNvShift);
+      for (int t = 0; KU * t < nv; ++t) dst[t] = hd | (t << kTileBits) | ((min(KU, nv - KU * t) - 1) << kUnitNvShift);
     }
     n_units = cols[4 * g.row_cap + 1];  // nu[1]
-    if (tid < ((4 - (n_units & 3)) & 3)) utab[n_units + tid] = cols[0] & ((1 << kTileBits) - 1);
+    if (tid < (UPC - n_units % UPC) % UPC) utab[n_units + tid] = cols[0] & ((1 << kTileBits) - 1);
   }
 
   typename C::WS ws;
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   // total chunks of the row (each wave sums the list on its own)
   int total = 0;
   if constexpr (UN) {
-    total = (n_units + 3) >> 2;
+    total = (n_units + UPC - 1) / UPC;
   } else {
     for (int e = lane; e < L; e += 64) total += (entry_nv(cols[e]) + kKC - 1) / kKC;
 #pragma unroll
@@ -460,10 +466,15 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     const int wsub = __builtin_amdgcn_readfirstlane(sub);
     auto issue_chunk = [&](int st, int nc) {
       UnitBases ub;
-      unit_bases<D>(utab[4 * nc + 0], slots, ub.k0, ub.v0);
-      unit_bases<D>(utab[4 * nc + 1], slots, ub.k1, ub.v1);
-      unit_bases<D>(utab[4 * nc + 2], slots, ub.k2, ub.v2);
-      unit_bases<D>(utab[4 * nc + 3], slots, ub.k3, ub.v3);
+      unit_bases<D, KU>(utab[UPC * nc + 0], slots, ub.k0, ub.v0);
+      unit_bases<D, KU>(utab[UPC * nc + 1], slots, ub.k1, ub.v1);
+      if constexpr (UPC == 4) {
+        unit_bases<D, KU>(utab[UPC * nc + 2], slots, ub.k2, ub.v2);
+        unit_bases<D, KU>(utab[UPC * nc + 3], slots, ub.k3, ub.v3);
+      } else {
+        ub.k2 = ub.k3 = ub.k0;  // never picked: units 0 and 1 only
+        ub.v2 = ub.v3 = ub.v0;
+      }
       ldr.issue_units(lds + st * Stage::STAGE, kt_head, vt_head, ub);
     };
 #pragma unroll
@@ -480,14 +491,21 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
       for (int u = 0; u < CPB; ++u) {
         if (c + u < total) {
           // valid keys of each unit for this wave's query tile
-          int n[4];
+          int n[UPC];
+          int any = 0;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int x = __builtin_amdgcn_readfirstlane(utab[4 * (c + u) + t]);
-            n[t] = ((x >> (kFlagShift + wsub)) & 1) ? (x >> kUnitNvShift) & 31 : 0;
+          for (int t = 0; t < UPC; ++t) {
+            const int x = __builtin_amdgcn_readfirstlane(utab[UPC * (c + u) + t]);
+            n[t] = ((x >> (kFlagShift + wsub)) & 1) ? ((x >> kUnitNvShift) & 31) + 1 : 0;
+            any += n[t];
           }
           const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
-          if (active && n[0] + n[1] + n[2] + n[3] > 0) ws.chunk_units(lk, lk + Stage::KE, n, c2, col, hi);
+          if (active && any > 0) {
+            if constexpr (C::kF8)
+              ws.chunk_units(lk, lk + Stage::KE, n[0], n[UPC - 1], c2, col, hi);
+            else
+              ws.chunk_units(lk, lk + Stage::KE, n, c2, col, hi);
+          }
         }
       }
     }
@@ -562,6 +580,8 @@ VSA_ATTEND_INST_C(F8Core<128>)
 VSA_ATTEND_INST_C(F8Core<64>)
 VSA_ATTEND_INST_UN(Bf16Core<128>)
 VSA_ATTEND_INST_UN(Bf16Core<64>)
+VSA_ATTEND_INST_UN(F8Core<128>)
+VSA_ATTEND_INST_UN(F8Core<64>)
 #undef VSA_ATTEND_INST_UN
 #undef VSA_ATTEND_INST_C
 #undef VSA_ATTEND_INST_U
@@ -623,9 +643,9 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
   const int nw = (slabs + groups - 1) / groups;
   // a pair of adjacent query tiles per workgroup (the plan decides; 4 to 6
   // waves per tile), when the ring and the lists fit in the CU's LDS
-  if constexpr (!C::kF8) {
-    // bf16 pairs cut the kept keys into 16-key units where the plan chose
-    // them, the table fits and the head's element offsets fit in 32 bits
+  {
+    // pairs cut the kept keys into 16-key (E4M3: 32-key) units where the plan
+    // chose them, the table fits and the head's element offsets fit in 32 bits
     if (g.blk[blocking].pair && g.blk[blocking].units && nw >= 4 && nw <= 6 &&
         attend_shmem<C, 4, 2, true>(g, blocking) <= 160 * 1024 && g.tok_cap * C::D <= 0x7fffffffL) {
       switch (nw) {

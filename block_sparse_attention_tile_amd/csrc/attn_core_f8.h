@@ -200,6 +200,22 @@ struct WaveState {
     pv(lvt, col, hi, p);
   }
 
+  // One staged chunk of two 32-key units (block b holds unit b) with n0, n1
+  // (0..32, wave-uniform, not both 0) valid keys.
+  __device__ __forceinline__ void chunk_units(const uint8_t* lk, const uint8_t* lvt, int n0, int n1,
+                                              float c2, int col, int hi) {
+    f32x16 s0 = scores(lk, 0, col, hi);
+    f32x16 s1 = scores(lk, 1, col, hi);
+    if (n0 < 32 || n1 < 32) {
+      mask(s0, n0, hi);
+      mask(s1, n1, hi);
+    }
+    int pk[8];
+    softmax(s0, s1, c2, pk);
+    const i32x8 p = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+    pv(lvt, col, hi, p);
+  }
+
   // Normalise (times oscale = 2^-e_v) and write this lane's query row (d
   // channels, bf16) to op.
   __device__ __forceinline__ void store(uint16_t* op, int hi, bool write, float oscale) const {

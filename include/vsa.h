@@ -181,14 +181,14 @@ typedef struct vsa_plan_info {
                                      kept lists (tiles of 4 to 6 slabs; Top-P masks, or
                                      static masks whose neighbours' lists mostly
                                      coincide) */
-  int32_t units[VSA_MAX_CAND];    /* 1: the bf16 attention of this paired blocking
-                                     stages the union's kept keys in 16-key units,
-                                     four per 64-key chunk across tile boundaries
-                                     (when that cuts the chunk count by 5% or more:
-                                     tile sizes not multiples of 64, ragged edge
-                                     tiles), unless the unit table does not fit in
-                                     LDS at launch; 0 without pairing and with
-                                     VSA_COMPUTE_FP8 */
+  int32_t units[VSA_MAX_CAND];    /* 1: the attention of this paired blocking stages
+                                     the union's kept keys in units of 16 keys (bf16)
+                                     or 32 keys (VSA_COMPUTE_FP8), packed into 64-key
+                                     chunks across tile boundaries (when that cuts the
+                                     chunk count by 5% or more: tile sizes not
+                                     multiples of 64, ragged edge tiles), unless the
+                                     unit table does not fit in LDS at launch; 0
+                                     without pairing */
 } vsa_plan_info;
 
 /* Workspace regions, for inspection by tests (see vsa_workspace_region). */

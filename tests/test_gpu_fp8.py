@@ -62,6 +62,9 @@ CASES = {
                            compute="fp8"),
     "seven_slab_ragged": Workload("seven_slab_ragged", 1, 2, 64, (5, 9, 30), (2, 8, 14), topp=0.9,
                                   compute="fp8"),
+    # paired 156-token tiles at d = 64: 32-key units (five per tile, the last with 28 keys),
+    # 12-token edge tiles
+    "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 13), topp=0.8, compute="fp8"),
 }
 
 
