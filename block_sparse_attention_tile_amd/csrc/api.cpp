@@ -7,9 +7,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "vsa_internal.h"
@@ -29,6 +32,24 @@ struct vsa_plan_s {
   size_t size[VSA_WS_NREGIONS];
   size_t ws_total;
 };
+
+namespace vsa {
+
+hipError_t ensure_dyn_lds(const void* kernel, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = raised[{dev, kernel}];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
+}
+
+}  // namespace vsa
 
 namespace {
 
@@ -689,6 +710,9 @@ int vsa_read_selection(const vsa_plan_t* p, const void* ws, size_t ws_bytes, int
     e = hipMemcpyAsync(cnd.data(), w.cand, BH * 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "reading the selection");
+  for (long bh = 0; bh < BH; ++bh)
+    if (cnd[bh] < 0 || cnd[bh] >= g.nb)
+      return fail(VSA_ERR_HIP, "corrupt blocking index %d for head %ld", cnd[bh], bh);
   int64_t n = 0;
   row_ptr[0] = 0;
   for (long r = 0; r < rows; ++r) {
@@ -749,6 +773,8 @@ int vsa_retained_work(const vsa_plan_t* p, const void* ws, size_t ws_bytes, int6
   int64_t pr = 0;
   double fl = 0;
   for (long bh = 0; bh < BH; ++bh) {
+    if (cnd[bh] < 0 || cnd[bh] >= g.nb)
+      return fail(VSA_ERR_HIP, "corrupt blocking index %d for head %ld", cnd[bh], bh);
     const BlkGeo& b = g.blk[cnd[bh]];
     std::vector<long> nv(b.n_tiles);
     for (int i = 0; i < b.n_tiles; ++i) nv[i] = tile_valid_id(g, b, i);

@@ -614,13 +614,9 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
   const long items = (long)g.B * g.H * units * nsb;
   const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
   const size_t shmem = attend_shmem<C, STAGES, TPW, UN>(g, blocking);
-  static size_t attr_bytes = 0;  // more than 64 KB of dynamic LDS must be requested
-  if (attr_bytes < shmem) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW, UN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_bytes = shmem;
-  }
+  // more than 64 KB of dynamic LDS must be requested (per device)
+  hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW, UN>), shmem);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attend_kernel<C, NW, STAGES, TPW, UN>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, reinterpret_cast<const T*>(w.qt), reinterpret_cast<const T*>(w.kt),
                      reinterpret_cast<const T*>(w.vt), w.row_len, w.col_idx, cand, w.f8_exp, o, nsb,

@@ -561,13 +561,8 @@ template <int D, int NW>
 hipError_t launch_fine_attend_t(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, uint16_t* o, hipStream_t s) {
   const size_t shmem = Lds<D>::STAGE * sizeof(uint16_t) + 2 * kKC * sizeof(int);  // stage, index buffers
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fine_attend_kernel<D, NW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(&fine_attend_kernel<D, NW>), shmem);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fine_attend_kernel<D, NW>), dim3(g.fine_G, g.B * g.H), dim3(NW * 64), shmem, s,
                      g, q, k, v, w.fine_ptr, w.fine_idx, o);
   return hipGetLastError();

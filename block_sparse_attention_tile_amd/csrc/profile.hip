@@ -575,18 +575,14 @@ template <int D>
 hipError_t launch_profile_d(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, hipStream_t s) {
   const size_t shmem = (size_t)FullLds<D>::TOTAL * sizeof(uint16_t);
-  static bool attr_set = false;  // more than 64 KB of dynamic LDS must be requested
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&profile_full_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // more than 64 KB of dynamic LDS must be requested (per device)
+  hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(&profile_full_kernel<D>), shmem);
+  if (e != hipSuccess) return e;
   float2* part_lm = reinterpret_cast<float2*>(w.prof_part);
   float* part_acc = w.prof_part + (size_t)g.B * g.H * g.prof_runs * g.prof_segs * kRun * 2;
   hipLaunchKernelGGL(profile_full_kernel<D>, dim3((g.prof_runs + kFullWaves - 1) / kFullWaves, g.B * g.H, g.prof_segs),
                      dim3(kFullWaves * 64), shmem, s, g, q, k, v, part_acc, part_lm);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(profile_masked_kernel<D>, dim3(g.prof_runs, g.B * g.H, g.nb), dim3(64), 0, s, g, q,
                      k, v, part_acc, part_lm, w.prof_sse);

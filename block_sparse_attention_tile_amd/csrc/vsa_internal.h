@@ -112,6 +112,10 @@ constexpr int kProfWaves = 12;
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.
 constexpr int kAmaxParts = 128;
 
+// Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device, once per (device, kernel); thread-safe (api.cpp).
+hipError_t ensure_dyn_lds(const void* kernel, size_t bytes);
+
 // Bytes of internal scratch the fine-grained mask needs (fine.hip).
 size_t fine_scratch_bytes(const Geo& g);
 
