@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     VSA_SUMM_MAX, VSA_SUMM_MEAN, VSA_SUMM_MINMAX, VSA_WIN_CLAMP, VSA_WIN_TRUNCATE, VsaError, lib,
     VSA_COMPUTE_BF16, VSA_COMPUTE_FP8, VSA_PROFILE_SELECT,
     make_policy, make_problem, vsa_attend,
-    vsa_forward, vsa_forward_cached, vsa_layout, vsa_plan, vsa_plan_destroy, vsa_plan_get_info,
+    vsa_forward, vsa_forward_cached, vsa_forward_noalloc, vsa_layout, vsa_plan, vsa_plan_destroy, vsa_plan_get_info,
     vsa_read_selection, vsa_retained_work, vsa_select, vsa_untile, vsa_workspace_bytes,
     vsa_workspace_region,
 )
@@ -89,6 +89,16 @@ class Plan:
         self._check(q, k, v, o)
         vsa_forward_cached(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(self.workspace()),
                            self.ws_bytes, self._stream())
+        return o
+
+    def forward_noalloc(self, q, k, v, o=None):
+        """Forward on the library's own per-device scratch array instead of
+        this plan's workspace: see vsa_forward_noalloc."""
+        import torch
+        if o is None:
+            o = torch.empty_like(q)
+        self._check(q, k, v, o)
+        vsa_forward_noalloc(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), self._stream())
         return o
 
     def layout(self, q, k, v):

@@ -35,6 +35,7 @@ VSA_SUMM_MAX = 1
 VSA_SUMM_MINMAX = 2
 VSA_COMPUTE_BF16 = 0
 VSA_COMPUTE_FP8 = 1
+VSA_NOALLOC_BYTES = 256 << 20
 
 (VSA_WS_QT, VSA_WS_KT, VSA_WS_VT, VSA_WS_POOLED_Q, VSA_WS_POOLED_K, VSA_WS_ROW_LEN,
  VSA_WS_COL_IDX, VSA_WS_CAND, VSA_WS_CAND_SCORE, VSA_WS_TILE_SICS, VSA_WS_ATOMS,
@@ -44,7 +45,8 @@ VSA_COMPUTE_FP8 = 1
 
 EXPORTED = [
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_workspace_bytes",
-    "vsa_workspace_region", "vsa_forward", "vsa_forward_cached", "vsa_layout", "vsa_select", "vsa_attend",
+    "vsa_workspace_region", "vsa_forward", "vsa_forward_cached", "vsa_forward_noalloc", "vsa_layout",
+    "vsa_select", "vsa_attend",
     "vsa_untile", "vsa_read_selection", "vsa_retained_work", "vsa_status_string",
     "vsa_last_error",
 ]
@@ -106,6 +108,7 @@ def lib():
         getattr(L, name).argtypes = [P, P, P, P, P, sz, P]
     for name in ("vsa_forward", "vsa_forward_cached", "vsa_attend"):
         getattr(L, name).argtypes = [P, P, P, P, P, P, sz, P]
+    L.vsa_forward_noalloc.argtypes = [P, P, P, P, P, P]
     L.vsa_untile.argtypes = [P, C.c_int, P, sz, P, P]
     L.vsa_read_selection.argtypes = [P, P, sz, C.POINTER(C.c_int32), C.POINTER(C.c_int32), sz,
                                      C.POINTER(C.c_int64), C.POINTER(C.c_int32), P]
@@ -203,6 +206,10 @@ def vsa_forward(plan, q, k, v, o, ws, ws_bytes, stream):
 
 def vsa_forward_cached(plan, q, k, v, o, ws, ws_bytes, stream):
     _check(lib().vsa_forward_cached(plan, q, k, v, o, ws, ws_bytes, stream))
+
+
+def vsa_forward_noalloc(plan, q, k, v, o, stream):
+    _check(lib().vsa_forward_noalloc(plan, q, k, v, o, stream))
 
 
 def vsa_layout(plan, q, k, v, ws, ws_bytes, stream):

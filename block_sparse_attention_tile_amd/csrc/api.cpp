@@ -51,6 +51,13 @@ hipError_t ensure_dyn_lds(const void* kernel, size_t bytes) {
 
 }  // namespace vsa
 
+// Device scratch of vsa_forward_noalloc.  One copy of this array exists on
+// every device the library's code object is loaded on, at that device's own
+// address, and stays until the process ends.  On the host its name is only a
+// stand-in: host code passes the address that hipGetSymbolAddress returns
+// for the current device (scratch_on_device below), never the name itself.
+static __device__ __align__(256) unsigned char scratch[vsa::kNoAllocBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -548,6 +555,32 @@ int check_device() {
   return VSA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255) != 0)
+      return fail(VSA_ERR_HIP, "scratch symbol address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -652,6 +685,28 @@ int vsa_forward(const vsa_plan_t* p, const void* q, const void* k, const void* v
       (st = check_tensor(o, "o")))
     return st;
   if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = enqueue_layout(p, q, k, v, ws, s))) return st;
+  if ((st = enqueue_select(p, q, k, ws, s))) return st;
+  if ((st = enqueue_attend(p, q, k, v, o, ws, s))) return st;
+  return ok();
+}
+
+int vsa_forward_noalloc(const vsa_plan_t* p, const void* q, const void* k, const void* v, void* o,
+                        void* stream) {
+  if (!p) return fail(VSA_ERR_INVALID_ARG, "plan is NULL");
+  if (p->ws_total > vsa::kNoAllocBytes)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "vsa_forward_noalloc: the plan needs %zu bytes of scratch, beyond the library's "
+                "fixed %zu bytes; use vsa_forward with a caller-provided workspace",
+                p->ws_total, vsa::kNoAllocBytes);
+  int st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(o, "o")))
+    return st;
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_on_device(&ws))) return st;
   hipStream_t s = (hipStream_t)stream;
   if ((st = enqueue_layout(p, q, k, v, ws, s))) return st;
   if ((st = enqueue_select(p, q, k, ws, s))) return st;

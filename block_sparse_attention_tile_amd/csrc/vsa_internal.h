@@ -112,6 +112,10 @@ constexpr int kProfWaves = 12;
 // Slices per (head, tensor) of the max |x| reduction of the FP8 path.
 constexpr int kAmaxParts = 128;
 
+// Bytes of the device array that vsa_forward_noalloc uses as its workspace
+// (api.cpp): plans needing more are refused by that entry point.
+constexpr size_t kNoAllocBytes = VSA_NOALLOC_BYTES;
+
 // Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
 // device, once per (device, kernel); thread-safe (api.cpp).
 hipError_t ensure_dyn_lds(const void* kernel, size_t bytes);

@@ -277,6 +277,22 @@ int vsa_forward(const vsa_plan_t* plan, const void* q, const void* k, const void
 int vsa_forward_cached(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                        void* o, void* workspace, size_t ws_bytes, void* stream);
 
+/* Forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same computation, arguments, ownership and errors
+ * as vsa_forward, except that the workspace is the library's own device
+ * array of VSA_NOALLOC_BYTES (256 MiB) per device, held until the process
+ * ends; nothing is allocated or freed by this call.  A plan whose
+ * vsa_workspace_bytes exceeds VSA_NOALLOC_BYTES is refused with
+ * VSA_ERR_UNSUPPORTED before anything is enqueued.  Every call on one device
+ * shares that device's array, which keeps the previous call's contents
+ * (each forward rewrites everything it reads): calls that overlap in time on
+ * one device (other streams, other threads) race and must be serialized by
+ * the caller. */
+#define VSA_NOALLOC_BYTES ((size_t)256 << 20)
+int vsa_forward_noalloc(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
+                        void* o, void* stream);
+
 /* Stage 1, layout: under VSA_SICS_SELECT scores every candidate blocking by
  * SICS (under VSA_PROFILE_SELECT by the sampled-row MSE) and records the
  * chosen one per head; then copies Q, K (tile-major)

@@ -261,3 +261,17 @@ def test_attention_units_where_tails_are_short():
     assert units(CONFIGS["tiny"]) == [0]
     assert units(Workload("u", 1, 2, 64, (4, 12, 40), (2, 6, 15), topp=0.8)) == [0]   # 180 = 12 units = 3 chunks
     assert units(Workload("u", 1, 2, 64, (4, 12, 40), (2, 6, 14), topp=0.8)) == [1]   # 168: 11 units < 3 chunks
+
+
+def test_noalloc_refuses_a_plan_beyond_its_scratch_without_touching_the_gpu():
+    # the size check comes before any device access, so this runs without a GPU
+    wl = CONFIGS["hunyuan"]
+    h = vsa.vsa_plan(*structs_of(wl))
+    assert vsa.vsa_workspace_bytes(h) > _lib.VSA_NOALLOC_BYTES
+    buf = (ctypes.c_char * 4096)()
+    p = (ctypes.addressof(buf) + 255) & ~255
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_forward_noalloc(h, p, p, p, p, None)
+    assert e.value.status == _lib.VSA_ERR_UNSUPPORTED
+    assert b"vsa_forward_noalloc" in vsa.lib().vsa_last_error()
+    vsa.vsa_plan_destroy(h)
