@@ -205,8 +205,7 @@ Ws resolve(const vsa_plan_t* p, void* ws) {
   w.fine_tau = (double*)at(VSA_WS_FINE_TAU);
   w.fine_count = (int*)at(VSA_WS_FINE_COUNT);
   w.fine_idx = (int*)at(VSA_WS_FINE_IDX);
-  w.fine_ptr = (int*)at(VSA_WS_FINE_PTR);
-  w.fine_score = (double*)at(VSA_WS_FINE_SCORE);
+  w.fine_mask = (uint32_t*)at(VSA_WS_FINE_MASK);
   w.scratch = (unsigned char*)at(VSA_WS_SCRATCH);
   w.f8_exp = (int*)at(VSA_WS_F8_EXP);
   w.f8_amax = (uint32_t*)at(VSA_WS_F8_AMAX);
@@ -307,7 +306,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       return fail(VSA_ERR_UNSUPPORTED, "groups*N = %ld exceeds 2^31 - 1", (long)g.fine_G * N);
     double total = (double)g.fine_G * (double)N;
     g.fine_keep = frac_count(po->fine_keep, (long)total);
-    g.fine_cap = std::min((long)total, g.fine_keep + N);
+    g.fine_cap = (long)g.fine_G * N;  // N keys per group: ties at the threshold may keep every pair
     g.nb = 0;
     g.max_tiles = 0;
     g.tok_cap = 0;
@@ -479,8 +478,7 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     sz[VSA_WS_FINE_TAU] = (size_t)BH * 8;
     sz[VSA_WS_FINE_COUNT] = (size_t)BH * g.fine_G * 4;
     sz[VSA_WS_FINE_IDX] = (size_t)BH * g.fine_cap * 4;
-    sz[VSA_WS_FINE_PTR] = (size_t)BH * (g.fine_G + 1) * 4;
-    sz[VSA_WS_FINE_SCORE] = (size_t)BH * g.fine_G * (size_t)N * 8;
+    sz[VSA_WS_FINE_MASK] = (size_t)BH * g.fine_G * (size_t)((N + 31) / 32) * 4;
   }
   sz[VSA_WS_SCRATCH] = (f & VSA_FINE) ? vsa::fine_scratch_bytes(g) : 256;
   size_t offv = 0;

@@ -42,7 +42,7 @@ struct Geo {
   // fine-grained mask
   int fine_M, fine_G;
   long fine_keep;   // kept (group, key) pairs per head (target count)
-  long fine_cap;    // kept-key list capacity per head
+  long fine_cap;    // kept-key list capacity per head: G*N (N per group)
   // SICS atoms: common refinement of the candidate blockings
   int atom[3];
   int na[3];
@@ -95,8 +95,7 @@ struct Ws {
   double* fine_tau;
   int* fine_count;
   int* fine_idx;
-  int* fine_ptr;
-  double* fine_score;
+  uint32_t* fine_mask;  // [B*H][G][ceil(N/32)] kept-pair bits
   unsigned char* scratch;
   int* f8_exp;          // [B*H][3] E4M3 scale exponents of Q, K, V
   uint32_t* f8_amax;    // [B*H][3][kAmaxParts] partial max |x| (bf16 bits)

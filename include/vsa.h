@@ -174,7 +174,9 @@ typedef struct vsa_plan_info {
                                      heads and batches; 0 if dynamic */
   int32_t fine_groups;            /* G for VSA_FINE, else 0 */
   int64_t fine_keep_count;        /* kept (group, key) pairs per head target */
-  int64_t fine_cap;               /* capacity of the kept-key list per head */
+  int64_t fine_cap;               /* capacity of the kept-key lists per head: G * N
+                                     (N per group, so ties at the threshold never
+                                     overflow) */
   double scale;                   /* resolved softmax scale */
   int32_t pair[VSA_MAX_CAND];     /* 1: the attention of this blocking runs two adjacent
                                      query tiles per workgroup over the union of their
@@ -206,9 +208,11 @@ typedef struct vsa_plan_info {
 #define VSA_WS_FINE_QBAR  11  /* fp32 [B*H][G][d] group means of Q */
 #define VSA_WS_FINE_TAU   12  /* fp64 [B*H] per-head score threshold */
 #define VSA_WS_FINE_COUNT 13  /* int32 [B*H][G] kept keys per group */
-#define VSA_WS_FINE_IDX   14  /* int32 [B*H][fine_cap] kept keys, groups in order */
-#define VSA_WS_FINE_PTR   15  /* int32 [B*H][G+1] start of each group's keys */
-#define VSA_WS_FINE_SCORE 16  /* fp64 [B*H][G][N] group-key scores */
+#define VSA_WS_FINE_IDX   14  /* int32 [B*H][G][N] kept keys of each group, ascending, in the
+                                 first FINE_COUNT entries of the group's row */
+#define VSA_WS_FINE_PTR   15  /* unused (0 bytes) */
+#define VSA_WS_FINE_MASK  16  /* uint32 [B*H][G][ceil(N/32)] kept (group, key) pairs, key j in bit
+                                 j % 32 of word j / 32 */
 #define VSA_WS_SCRATCH    17  /* internal */
 #define VSA_WS_POOLED_KMIN 18 /* fp32 [B*H][d][max_tiles] (channel-major) per-channel K minimum (VSA_SUMM_MINMAX) */
 #define VSA_WS_F8_EXP     19  /* int32 [B*H][3] exponents e_q, e_k, e_v (VSA_COMPUTE_FP8) */

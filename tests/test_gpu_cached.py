@@ -14,7 +14,7 @@ import block_sparse_attention_tile_amd as vsa
 from block_sparse_attention_tile_amd import _lib
 from oracle import attention, fine, geometry
 from synth import Workload, smooth_field_qkv
-from tests.helpers import csr_rows, structs_of
+from tests.helpers import csr_rows, oracle_candidate, oracle_tile_rows, structs_of, unambiguous
 
 pytestmark = pytest.mark.gpu
 ATOL = 2e-2
@@ -62,9 +62,17 @@ def test_cached_mask_reused_on_new_input(name):
     for b in range(wl.B):
         for h in range(wl.H):
             bh = b * wl.H + h
+            # A's selection is the oracle's on A (Top-P rows at the rounding margin excepted)
+            qa_h, ka_h = (t[b, h].float().cpu().numpy() for t in (qa, ka))
+            if wl.candidates:
+                c_ref, _ = oracle_candidate(wl, qa_h, ka_h)
+                assert int(cand_a[bh]) == c_ref, (bh, int(cand_a[bh]), c_ref)
             tile = tiles[int(cand_a[bh])] if wl.candidates else wl.tile
             mem = geometry.tile_members(wl.grid, tile)
             rows = csr_rows(rp_a, col_a, bh, mt, len(mem))
+            rows_ref, margins, _ = oracle_tile_rows(wl, qa_h, ka_h, tile)
+            for i in unambiguous(range(len(mem)), margins):
+                assert rows[i] == list(rows_ref[i]), (bh, i)
             qn, kn, vn = (t[b, h].float().cpu().numpy() for t in (qb, kb, vb))
             ref = attention.block_sparse_attention(qn, kn, vn, mem, rows)
             worst = max(worst, float(np.abs(ob[b, h].float().cpu().numpy() - ref).max()))
@@ -79,16 +87,20 @@ def test_cached_fine_mask_reused_on_new_input():
     qb, kb, vb = _inputs(wl, 7)
     plan.forward(qa, ka, va)
     torch.cuda.synchronize()
-    BH, G = wl.B * wl.H, plan.info.fine_groups
-    ptr = plan.region(_lib.VSA_WS_FINE_PTR, torch.int32).view(BH, G + 1).cpu().numpy().copy()
-    idx = plan.region(_lib.VSA_WS_FINE_IDX, torch.int32).view(BH, -1).cpu().numpy().copy()
+    BH, G, N = wl.B * wl.H, plan.info.fine_groups, wl.N
+    count = plan.region(_lib.VSA_WS_FINE_COUNT, torch.int32).view(BH, G).cpu().numpy().copy()
+    idx = plan.region(_lib.VSA_WS_FINE_IDX, torch.int32).view(BH, G, N).cpu().numpy().copy()
     ob = plan.forward_cached(qb, kb, vb)
     torch.cuda.synchronize()
-    assert np.array_equal(ptr, plan.region(_lib.VSA_WS_FINE_PTR, torch.int32).view(BH, G + 1).cpu().numpy())
-    N = wl.N
+    assert np.array_equal(count, plan.region(_lib.VSA_WS_FINE_COUNT, torch.int32).view(BH, G).cpu().numpy())
     grp = fine.groups(N, wl.fine_group)
     for bh in range(BH):
-        lists = [idx[bh, ptr[bh, g]:ptr[bh, g + 1]] for g in range(G)]
+        lists = [idx[bh, g, :count[bh, g]] for g in range(G)]
+        # A's mask is the oracle's on A
+        s_a = fine.group_scores(fine.group_means(qa[0, bh].float().cpu().numpy(), wl.fine_group),
+                                ka[0, bh].float().cpu().numpy())
+        ref_lists = fine.kept_lists(s_a, fine.threshold(s_a, fine.keep_count(wl.fine_keep, G, N)))
+        assert all(np.array_equal(a, r) for a, r in zip(lists, ref_lists)), bh
         qn, kn, vn = (t[0, bh].float().cpu().numpy() for t in (qb, kb, vb))
         ref = attention.fine_attention(qn, kn, vn, grp, lists)
         err = float(np.abs(ob[0, bh].float().cpu().numpy() - ref).max())
