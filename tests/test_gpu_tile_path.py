@@ -128,12 +128,20 @@ def test_pooled_means_bit_exact(name):
                     assert np.array_equal(pkn[b * wl.H + h], kmin)
 
 
+# (pair, units) the plan must choose for the cases that exist to run the
+# paired / unit kernels (and for two that must not)
+KERNELS = {"w480_mini": (1, 1), "pair_window_odd": (1, 1), "pair_units_105": (1, 1),
+           "pair_units_d64": (1, 1), "eleven_slab_units": (0, 0), "hy_mini": (0, 0)}
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_selection_and_attention_small(name):
     wl = SMALL[name]
     _say(f"forward {name}")
     q, k, v = _inputs(wl)
     plan, o = _run_all(wl, q, k, v)
+    if name in KERNELS:
+        assert (plan.info.pair[0], plan.info.units[0]) == KERNELS[name]
     row_ptr, col, _ = plan.read_selection()
     qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
     on = o.float().cpu().numpy()

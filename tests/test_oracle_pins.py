@@ -483,3 +483,29 @@ def test_default_scale():
     assert select.default_scale(64) == 0.125
     assert select.default_scale(128) == 1.0 / math.sqrt(128.0)
     assert math.isclose(select.default_scale(128) ** 2 * 128, 1.0, rel_tol=1e-15)
+
+
+def test_candidate_scores_worked_example():
+    """Two blockings of different block sizes on a 1 x 1 x 4 grid (d = 2),
+    worked out by hand.  Tokens 0, 1 are e1; tokens 2, 3 are at 60 degrees to
+    e1.  Blocking 0 (1x1x2) has tiles {0,1}, {2,3}: pair cosines 1 and 1, mean
+    pair cosine 1, SICS sum 2.  Blocking 1 (1x1x4) has one tile: pair cosines
+    1, 1 and four times 0.5, SICS 4, mean pair cosine 4/6.
+
+    With K = Q the score is the mean pair cosine, [1, 2/3]: blocking 0 wins,
+    while a raw SICS sum (2 vs 4, or its mean over tiles, 1 vs 4) would pick
+    blocking 1.  With K = (e1, -e1, e1, -e1) the K mean pair cosines are -1
+    (tiles {0,1}, {2,3}) and -2/6 (one tile: four pairs at -1, two at +1), so
+    the averaged scores are [0, 1/6] and blocking 1 wins, while Q alone would
+    still pick blocking 0."""
+    grid = (1, 1, 4)
+    cands = ((1, 1, 2), (1, 1, 4))
+    c60 = (0.5, math.sqrt(3.0) / 2.0)
+    q = np.array([[1.0, 0.0], [1.0, 0.0], c60, c60])
+    sc = sics.candidate_scores(q, q, grid, cands)
+    assert np.allclose(sc, [1.0, 2.0 / 3.0], rtol=0, atol=1e-12), sc
+    assert sics.choose(sc) == 0
+    k = np.array([[1.0, 0.0], [-1.0, 0.0], [1.0, 0.0], [-1.0, 0.0]])
+    sc = sics.candidate_scores(q, k, grid, cands)
+    assert np.allclose(sc, [0.0, 1.0 / 6.0], rtol=0, atol=1e-12), sc
+    assert sics.choose(sc) == 1
