@@ -107,11 +107,54 @@ def _cpu_baseline(wl, q, k, v, budget_s):
         if dt > budget_s:
             break
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host_cores": os.cpu_count(), "cpu_model": _cpu_model(),
             "sample": f"{done} query tiles of {nT} per head over {heads} head(s) "
                       f"({done * len(mem[0])} query rows), fp64 numpy masked-softmax "
                       f"attention; {dt:.1f} s; {flops:.3e} retained FLOPs",
             "ms_per_call_extrapolated": dt / flops * (sum(head_flops) / len(head_flops)) * wl.B * wl.H * 1e3}
+
+
+def _cpu_model():
+    """The host CPU's model name (lscpu), for the CPU baseline's record."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    return None
+
+
+def _copy_gbs(dev, stage):
+    """Device-to-device copy of 1 GiB (torch copy_) in the same run: the
+    practical ceiling of a read+write HBM stream on this part."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    ms = stage(lambda: b.copy_(a), 10)
+    del a, b
+    return 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+def _clamp_leg(wl, q, k, v, o, n, stage):
+    """The same static workload with the window clamped at the grid edge
+    (every window keeps its full 3x3x5 size: 13,500 tile pairs per head at
+    HunyuanVideo instead of 9,152)."""
+    import block_sparse_attention_tile_amd as vsa
+    from block_sparse_attention_tile_amd.workload import plan_structs
+    print("[bench] clamped-window leg", file=sys.stderr, flush=True)
+    plan_c = vsa.Plan(*plan_structs(wl.with_(win_mode="clamp")))
+    ms_call = stage(lambda: plan_c.forward(q, k, v, o), n)
+    ms_attend = stage(lambda: plan_c.attend(o, q, k, v), n)
+    pairs, flops = plan_c.retained_work()
+    return {"mask": _mask_desc(wl.with_(win_mode="clamp")), "retained_pairs": pairs,
+            "retained_flops": flops, "ms_per_call": round(ms_call, 4),
+            "attend_ms": round(ms_attend, 4),
+            "value": round(flops / (ms_call * 1e-3) / 1e12, 2),
+            "attend_tflops": round(flops / (ms_attend * 1e-3) / 1e12, 2),
+            "attend_frac": round(flops / (ms_attend * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def main():
@@ -127,6 +170,8 @@ def main():
     ap.add_argument("--sink", type=int, default=None, help="override the workload's sink tiles")
     ap.add_argument("--compute", choices=["bf16", "fp8"], default=None,
                     help="override the attention arithmetic (fp8 = E4M3 Q, K, V and probabilities)")
+    ap.add_argument("--no-clamp-leg", action="store_true",
+                    help="skip the clamped-window measurement of a static-window workload")
     ap.add_argument("--no-fp8-leg", action="store_true",
                     help="skip the E4M3 (VSA_COMPUTE_FP8) measurement of the same workload")
     ap.add_argument("--copy-calib", action="store_true",
@@ -221,6 +266,11 @@ def main():
     fp8_leg = None
     if not f8 and not wl.fine_group and not args.no_fp8_leg:
         fp8_leg = _fp8_leg(wl, q, k, v, o, n_st, stage, flops)
+    clamp_leg = None
+    if wl.window and wl.win_mode == "truncate" and not (wl.topk or wl.topk_frac or wl.topp) \
+            and not wl.candidates and not f8 and not args.no_clamp_leg:
+        clamp_leg = _clamp_leg(wl, q, k, v, o, n_st, stage)
+    copy_gbs = None if wl.fine_group else _copy_gbs(dev, stage)
 
     choice = None
     if wl.candidates:  # heads per chosen blocking (SICS or profiling selector)
@@ -260,10 +310,14 @@ def main():
         "layout_gbs": round(bytes_layout / (ms_layout * 1e-3) / 1e9, 1) if bytes_layout else None,
         "layout_hbm_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                             if bytes_layout else None),
+        "hbm_copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
+        "layout_copy_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / copy_gbs, 4)
+                             if bytes_layout and copy_gbs else None),
         "attend_tflops": round(attn_tflops, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "fp8": fp8_leg,
+        "clamp_window": clamp_leg,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

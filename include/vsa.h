@@ -228,6 +228,13 @@ typedef struct vsa_plan_info {
  * multiplies are then contiguous. */
 
 /* ---- plan ---------------------------------------------------------------
+ * The policy (candidate blockings, mask expressions and budgets) is fixed
+ * here, ahead of and apart from the execution calls (SPADE review page, "What
+ * carries the argument": the specification of 3D blocking candidates and
+ * summarizer / estimator masks, scheme generation, and a separate sparse
+ * executor; "If this is right": policy separated from mechanism).  A tile is
+ * a 3D box of tokens kept consecutive (STA verdict page,
+ * pith_extraction.key_machinery).
  * Validates `prob` and `pol`, computes the tile geometry of every blocking,
  * the static window statistics and the workspace layout.  Host only: makes
  * no HIP call and needs no GPU.  On success *out owns a plan that the caller
@@ -297,7 +304,12 @@ int vsa_forward_cached(const vsa_plan_t* plan, const void* q, const void* k, con
 int vsa_forward_noalloc(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                         void* o, void* stream);
 
-/* Stage 1, layout: under VSA_SICS_SELECT scores every candidate blocking by
+/* Stage 1, layout (the token-to-tile layout transform, fused with the block
+ * summaries as on the SPADE review page, "What carries the argument"; tiles
+ * kept consecutive in memory, STA verdict page, pith_extraction.key_machinery;
+ * per-head blocking choice by SICS, SPADE "Core claim", or by the sampled-row
+ * profiler, Sparse VideoGen verdict page, pith_extraction.key_machinery).
+ * Under VSA_SICS_SELECT scores every candidate blocking by
  * SICS (under VSA_PROFILE_SELECT by the sampled-row MSE) and records the
  * chosen one per head; then copies Q, K (tile-major)
  * and V (tile-major, transposed per tile) into the workspace, padding each
@@ -306,14 +318,22 @@ int vsa_forward_noalloc(const vsa_plan_t* plan, const void* q, const void* k, co
 int vsa_layout(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                void* workspace, size_t ws_bytes, void* stream);
 
-/* Stage 2, selection: the kept key tiles of every query tile (ascending,
+/* Stage 2, selection (block scores from the summaries, then Top-K / Top-P
+ * united with the sliding tile window and the sink: SPADE review page, "Core
+ * claim" and Figure 4; STA verdict page, pith_extraction.pith_summary; or the
+ * per-head quantile of the M x 1 group mask: FG-Attn verdict page,
+ * referee_report.major_comments[1]): the kept key tiles of every query tile (ascending,
  * in the workspace's ROW_LEN / COL_IDX regions), or under VSA_FINE the kept
  * keys of every query group.  Reads q, k only under VSA_FINE. */
 int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                void* workspace, size_t ws_bytes, void* stream);
 
-/* Stage 3, attention: block-sparse (or fine-grained) attention with online
- * softmax, fp32 accumulation, bf16 output written straight to raster `o`.
+/* Stage 3, attention (dense MFMA work on every kept block, the mask kept out
+ * of the inner loop: STA verdict page, pith_extraction.key_machinery; online
+ * softmax: SPADE review page, ledger axiom; gathered M x 1 slices: FG-Attn
+ * verdict page, pith_extraction.key_machinery): block-sparse (or
+ * fine-grained) attention with online softmax, fp32 accumulation, bf16
+ * output written straight to raster `o`.
  * Requires stages 1 and 2 on the same workspace. */
 int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                void* o, void* workspace, size_t ws_bytes, void* stream);
@@ -325,6 +345,11 @@ int vsa_untile(const vsa_plan_t* plan, int which, const void* workspace, size_t 
                void* out, void* stream);
 
 /* ---- debug getters (synchronize `stream`) -------------------------------
+ * vsa_read_selection returns the block mask that vsa_select built (the kept
+ * key tiles of each query tile: SPADE review page, "Core claim"; STA verdict
+ * page, pith_extraction.pith_summary).  The pooled summaries and SICS values
+ * are not copied by it: they are read through vsa_workspace_region
+ * (VSA_WS_POOLED_Q / _K / _KMIN, VSA_WS_TILE_SICS, VSA_WS_CAND_SCORE).
  * Copies the tile selection to host memory as CSR over rows r = (b*H + h) *
  * max_tiles + i: row_ptr has B*H*max_tiles + 1 entries, col_idx capacity
  * col_cap entries (B*H*max_tiles*row_cap always suffices); *n_kept receives
