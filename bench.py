@@ -252,10 +252,13 @@ def main():
     ms_cached = stage(lambda: plan.forward_cached(q, k, v, o), n_st)
 
     BH = wl.B * wl.H
-    # read Q, K, V + write the tile-major copies (no layout stage for the
-    # fine-grained mask, which reads the raster tensors directly)
-    # (E4M3: one more read of Q, K, V for the per-head maxima, 1-byte writes)
-    bytes_layout = 0.0 if wl.fine_group else BH * wl.N * wl.d * (15.0 if f8 else 12.0)
+    # bf16: read K, V (and Q for dynamic masks' summaries) + write tile-major K
+    # and V^T (the attention reads Q in raster order); E4M3: read Q, K, V for
+    # the per-head maxima, again for the 1-byte tile-major copies of all three.
+    # No layout stage for the fine-grained mask (it reads the raster tensors).
+    pool = bool(wl.topk or wl.topk_frac or wl.topp)
+    per_tok = 15.0 if f8 else (10.0 if pool else 8.0)
+    bytes_layout = 0.0 if wl.fine_group else BH * wl.N * wl.d * per_tok
     attn_tflops = flops / (ms_attend * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
     traffic = _traffic("attend_fp8" if f8 else "attend", wl.name)

@@ -451,7 +451,9 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
   size_t sz[VSA_WS_NREGIONS] = {0};
   if (!(f & VSA_FINE)) {
     size_t tm = (size_t)BH * g.tok_cap * g.d * 2;
-    sz[VSA_WS_QT] = sz[VSA_WS_KT] = sz[VSA_WS_VT] = tm;
+    sz[VSA_WS_KT] = sz[VSA_WS_VT] = tm;
+    // bf16 attention reads Q in raster order: tile-major Q only for E4M3
+    sz[VSA_WS_QT] = g.f8 ? tm : 0;
     if (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) {
       sz[VSA_WS_POOLED_Q] = sz[VSA_WS_POOLED_K] = (size_t)BH * g.max_tiles * g.d * 4;
       if (g.summ == VSA_SUMM_MINMAX) sz[VSA_WS_POOLED_KMIN] = sz[VSA_WS_POOLED_K];
@@ -541,7 +543,7 @@ int enqueue_attend(const vsa_plan_t* p, const void* q, const void* k, const void
     e = vsa::launch_fine_attend(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                 (uint16_t*)o, s);
   else
-    e = vsa::launch_attend(g, w, (uint16_t*)o, s);
+    e = vsa::launch_attend(g, w, (const uint16_t*)q, (uint16_t*)o, s);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return VSA_OK;
 }
@@ -669,6 +671,8 @@ int vsa_attend(const vsa_plan_t* p, const void* q, const void* k, const void* v,
   if (p->geo.flags & VSA_FINE) {
     if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")))
       return st;
+  } else if (!p->geo.f8) {
+    if ((st = check_tensor(q, "q"))) return st;  // bf16 attention reads q in raster order
   }
   if ((st = check_device())) return st;
   st = enqueue_attend(p, q, k, v, o, ws, (hipStream_t)stream);
@@ -733,6 +737,8 @@ int vsa_untile(const vsa_plan_t* p, int which, const void* ws, size_t ws_bytes, 
   if (p->geo.flags & VSA_FINE) return fail(VSA_ERR_UNSUPPORTED, "no tiled layout under VSA_FINE");
   if (p->geo.f8) return fail(VSA_ERR_UNSUPPORTED, "the tiled layout holds E4M3 under VSA_COMPUTE_FP8");
   if (which != 0 && which != 1) return fail(VSA_ERR_INVALID_ARG, "which must be 0 (Q) or 1 (K)");
+  if (which == 0)
+    return fail(VSA_ERR_UNSUPPORTED, "no tile-major Q: the bf16 attention reads Q in raster order");
   if ((st = check_tensor(out, "out"))) return st;
   if ((st = check_device())) return st;
   Ws w = resolve(p, (void*)ws);

@@ -22,6 +22,9 @@
 //    (bf16) and attn_core_f8.h (E4M3, VSA_COMPUTE_FP8: Sparse VideoGen
 //    verdict page, optional FP8 attention; per-head power-of-two scales
 //    from the layout stage).
+//  * bf16: each wave reads its 32 query rows straight from the raster input
+//    (once per workgroup, so the tile permutation costs nothing there); the
+//    layout stage copies only K and V^T.
 //  * The epilogue writes O straight to the raster layout (the inverse
 //    permutation is fused here), skipping padded query slots.
 //  * Workgroups are mapped XCD-major: consecutive work items (same head,
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     Geo g, int blocking, const typename C::T* __restrict__ qt, const typename C::T* __restrict__ kt,
     const typename C::T* __restrict__ vt, const int* __restrict__ row_len,
     const int* __restrict__ col_idx, const int* __restrict__ cand, const int* __restrict__ f8_exp,
-    uint16_t* __restrict__ o, int nsb, int n_items) {
+    uint16_t* __restrict__ o, int nsb, int n_items, const uint16_t* __restrict__ qr) {
   constexpr int D = C::D;
   using T = typename C::T;
   using Stage = typename C::L;
@@ -423,7 +426,14 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   }
 
   typename C::WS ws;
-  if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
+  if constexpr (C::kF8) {
+    if (active) ws.init(qt + head_tm + ((long)i * slots + qrow + col) * D, hi);
+  } else if (active) {
+    // bf16: the lane's query row straight from the raster input (a padded
+    // slot re-reads the tile's last token; its output is never stored)
+    const TileInfo tq = tinfo(g, b, i);
+    ws.init(qr + (bh * (long)g.N + token_of(g, b, tq, min(qrow + col, tq.nvalid - 1))) * D, hi);
+  }
   float c2 = (float)(g.scale * 1.4426950408889634);  // scale * log2(e)
   float oscale = 1.f;
   if constexpr (C::kF8) {
@@ -565,7 +575,7 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   template __global__ void attend_kernel<C, NW, ST, TPW, UN>(Geo, int, const typename C::T*,  \
                                                     const typename C::T*, const typename C::T*, \
                                                     const int*, const int*, const int*,        \
-                                                    const int*, uint16_t*, int, int);
+                                                    const int*, uint16_t*, int, int, const uint16_t*);
 #define VSA_ATTEND_INST_C(C)                                                               \
   VSA_ATTEND_INST(C, 1, 2) VSA_ATTEND_INST(C, 2, 2) VSA_ATTEND_INST(C, 3, 2)    \
   VSA_ATTEND_INST(C, 4, 2) VSA_ATTEND_INST(C, 5, 2) VSA_ATTEND_INST(C, 6, 2)    \
@@ -604,8 +614,8 @@ size_t attend_shmem(const Geo& g, int blocking) {
 }
 
 template <class C, int NW, int STAGES, int TPW = 1, bool UN = false>
-hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
-                      hipStream_t s) {
+hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, const uint16_t* q,
+                      uint16_t* o, hipStream_t s) {
   using T = typename C::T;
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
@@ -620,13 +630,13 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
   hipLaunchKernelGGL((attend_kernel<C, NW, STAGES, TPW, UN>), dim3(per_xcd * kNumXcd), dim3(NW * 64), shmem, s,
                      g, blocking, reinterpret_cast<const T*>(w.qt), reinterpret_cast<const T*>(w.kt),
                      reinterpret_cast<const T*>(w.vt), w.row_len, w.col_idx, cand, w.f8_exp, o, nsb,
-                     (int)items);
+                     (int)items, q);
   return hipGetLastError();
 }
 
 template <class C>
-hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, uint16_t* o,
-                    hipStream_t s) {
+hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, const uint16_t* q,
+                    uint16_t* o, hipStream_t s) {
   // Waves per workgroup: the tile's 32-row slabs split into as few balanced
   // groups of at most kMaxWaves as possible.  At 3 waves per SIMD a CU holds
   // 12 waves, so groups of 7 to 12 waves run one workgroup per CU; groups of
@@ -645,48 +655,48 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, ui
     if (g.blk[blocking].pair && g.blk[blocking].units && nw >= 4 && nw <= 6 &&
         attend_shmem<C, 4, 2, true>(g, blocking) <= 160 * 1024 && g.tok_cap * C::D <= 0x7fffffffL) {
       switch (nw) {
-        case 4: return launch_one<C, 8, 4, 2, true>(g, w, blocking, cand, o, s);
-        case 5: return launch_one<C, 10, 4, 2, true>(g, w, blocking, cand, o, s);
-        default: return launch_one<C, 12, 4, 2, true>(g, w, blocking, cand, o, s);
+        case 4: return launch_one<C, 8, 4, 2, true>(g, w, blocking, cand, q, o, s);
+        case 5: return launch_one<C, 10, 4, 2, true>(g, w, blocking, cand, q, o, s);
+        default: return launch_one<C, 12, 4, 2, true>(g, w, blocking, cand, q, o, s);
       }
     }
   }
   if (g.blk[blocking].pair && nw >= 4 && nw <= 6 && attend_shmem<C, 4, 2>(g, blocking) <= 160 * 1024) {
     switch (nw) {
-      case 4: return launch_one<C, 8, 4, 2>(g, w, blocking, cand, o, s);
-      case 5: return launch_one<C, 10, 4, 2>(g, w, blocking, cand, o, s);
-      default: return launch_one<C, 12, 4, 2>(g, w, blocking, cand, o, s);
+      case 4: return launch_one<C, 8, 4, 2>(g, w, blocking, cand, q, o, s);
+      case 5: return launch_one<C, 10, 4, 2>(g, w, blocking, cand, q, o, s);
+      default: return launch_one<C, 12, 4, 2>(g, w, blocking, cand, q, o, s);
     }
   }
   switch (nw) {
-    case 1: return launch_one<C, 1, 2>(g, w, blocking, cand, o, s);
-    case 2: return launch_one<C, 2, 2>(g, w, blocking, cand, o, s);
-    case 3: return launch_one<C, 3, 2>(g, w, blocking, cand, o, s);
-    case 4: return launch_one<C, 4, 2>(g, w, blocking, cand, o, s);
-    case 5: return launch_one<C, 5, 2>(g, w, blocking, cand, o, s);
-    case 6: return launch_one<C, 6, 2>(g, w, blocking, cand, o, s);
-    case 7: return C::kF8 ? launch_one<C, 7, 4>(g, w, blocking, cand, o, s) : launch_one<C, 7, 2>(g, w, blocking, cand, o, s);
-    case 8: return C::kF8 ? launch_one<C, 8, 4>(g, w, blocking, cand, o, s) : launch_one<C, 8, 2>(g, w, blocking, cand, o, s);
-    case 9: return launch_one<C, 9, 4>(g, w, blocking, cand, o, s);
-    case 10: return launch_one<C, 10, 4>(g, w, blocking, cand, o, s);
-    case 11: return launch_one<C, 11, 4>(g, w, blocking, cand, o, s);
-    default: return launch_one<C, 12, 4>(g, w, blocking, cand, o, s);
+    case 1: return launch_one<C, 1, 2>(g, w, blocking, cand, q, o, s);
+    case 2: return launch_one<C, 2, 2>(g, w, blocking, cand, q, o, s);
+    case 3: return launch_one<C, 3, 2>(g, w, blocking, cand, q, o, s);
+    case 4: return launch_one<C, 4, 2>(g, w, blocking, cand, q, o, s);
+    case 5: return launch_one<C, 5, 2>(g, w, blocking, cand, q, o, s);
+    case 6: return launch_one<C, 6, 2>(g, w, blocking, cand, q, o, s);
+    case 7: return C::kF8 ? launch_one<C, 7, 4>(g, w, blocking, cand, q, o, s) : launch_one<C, 7, 2>(g, w, blocking, cand, q, o, s);
+    case 8: return C::kF8 ? launch_one<C, 8, 4>(g, w, blocking, cand, q, o, s) : launch_one<C, 8, 2>(g, w, blocking, cand, q, o, s);
+    case 9: return launch_one<C, 9, 4>(g, w, blocking, cand, q, o, s);
+    case 10: return launch_one<C, 10, 4>(g, w, blocking, cand, q, o, s);
+    case 11: return launch_one<C, 11, 4>(g, w, blocking, cand, q, o, s);
+    default: return launch_one<C, 12, 4>(g, w, blocking, cand, q, o, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s) {
+hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s) {
   const int* cand = per_head_blocking(g) ? w.cand : nullptr;
   // One launch per blocking (heads grouped by their chosen blocking); a
   // workgroup whose head chose another blocking exits at once.
   for (int c = 0; c < g.nb; ++c) {
     hipError_t e;
     if (g.f8)
-      e = (g.d == 128) ? launch_d<F8Core<128>>(g, w, c, cand, o, s) : launch_d<F8Core<64>>(g, w, c, cand, o, s);
+      e = (g.d == 128) ? launch_d<F8Core<128>>(g, w, c, cand, q, o, s) : launch_d<F8Core<64>>(g, w, c, cand, q, o, s);
     else
-      e = (g.d == 128) ? launch_d<Bf16Core<128>>(g, w, c, cand, o, s)
-                       : launch_d<Bf16Core<64>>(g, w, c, cand, o, s);
+      e = (g.d == 128) ? launch_d<Bf16Core<128>>(g, w, c, cand, q, o, s)
+                       : launch_d<Bf16Core<64>>(g, w, c, cand, q, o, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

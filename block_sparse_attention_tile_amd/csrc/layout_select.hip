@@ -212,8 +212,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
     kmn[x] = INFINITY;
   }
   const bool extrema = pool && g.summ != VSA_SUMM_MEAN;
-
-  // Q and K: gather raster rows, store contiguous tile-major rows.
+  // Q and K: gather raster rows, store contiguous tile-major rows (Q only for
+  // E4M3: the bf16 attention reads Q in raster order).
   for (int s0 = r0; s0 < b.slots; s0 += RPP * U) {
     uint4 qv[U], kv[U];
 #pragma unroll
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
       kv[u] = qv[u];
       if (s < t.nvalid) {
         const long off = in_base + token_of(g, b, t, s) * D + p * 8;
-        qv[u] = *reinterpret_cast<const uint4*>(q + off);
+        if (F8 || pool) qv[u] = *reinterpret_cast<const uint4*>(q + off);  // bf16: summaries only
         kv[u] = *reinterpret_cast<const uint4*>(k + off);
       }
     }
@@ -235,7 +235,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(
           *reinterpret_cast<uint2*>(qt8 + tm_base + (long)s * D + p * 8) = quant8(qv[u], eq);
           *reinterpret_cast<uint2*>(kt8 + tm_base + (long)s * D + p * 8) = quant8(kv[u], ek);
         } else {
-          *reinterpret_cast<uint4*>(qt + tm_base + (long)s * D + p * 8) = qv[u];
           *reinterpret_cast<uint4*>(kt + tm_base + (long)s * D + p * 8) = kv[u];
         }
       }

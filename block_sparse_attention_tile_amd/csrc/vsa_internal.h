@@ -132,7 +132,8 @@ hipError_t launch_amax(const Geo& g, const Ws& w, const uint16_t* q, const uint1
                        const uint16_t* v, hipStream_t s);
 hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s);
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s);
-hipError_t launch_attend(const Geo& g, const Ws& w, uint16_t* o, hipStream_t s);
+// (bf16 attention reads its query rows from the raster q)
+hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s);
 hipError_t launch_sics(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                        hipStream_t s);
 // Profiling selector: per-head MSE of every candidate on the sampled rows,

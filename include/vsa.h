@@ -194,7 +194,8 @@ typedef struct vsa_plan_info {
 } vsa_plan_info;
 
 /* Workspace regions, for inspection by tests (see vsa_workspace_region). */
-#define VSA_WS_QT          0  /* bf16 [B*H][tiles*slots][d] tile-major Q */
+#define VSA_WS_QT          0  /* tile-major Q, VSA_COMPUTE_FP8 only (0 bytes under bf16: the bf16
+                                 attention reads Q in raster order) */
 #define VSA_WS_KT          1  /* bf16 [B*H][tiles*slots][d] tile-major K */
 #define VSA_WS_VT          2  /* bf16 [B*H][tiles][d][slots] tile-major V, transposed per tile */
 #define VSA_WS_POOLED_Q    3  /* fp32 [B*H][max_tiles][d] mean of Q */
@@ -337,10 +338,14 @@ int vsa_select(const vsa_plan_t* plan, const void* q, const void* k, const void*
  * Requires stages 1 and 2 on the same workspace. */
 int vsa_attend(const vsa_plan_t* plan, const void* q, const void* k, const void* v,
                void* o, void* workspace, size_t ws_bytes, void* stream);
+/* (vsa_attend reads q, k, v under VSA_FINE, and q under bf16 tile masks, whose
+ * attention reads the query rows in raster order; otherwise they may be NULL.) */
 
-/* Inverse layout: copy the workspace's tile-major Q (which = 0) or K
- * (which = 1) back to raster bf16 [B, H, N, d] in `out`, dropping pads.
- * VSA_ERR_UNSUPPORTED under VSA_COMPUTE_FP8 (the workspace holds E4M3). */
+/* Inverse layout: copy the workspace's tile-major K (which = 1) back to
+ * raster bf16 [B, H, N, d] in `out`, dropping pads.  which = 0 (Q) is
+ * VSA_ERR_UNSUPPORTED: the bf16 attention reads Q in raster order, so no
+ * tile-major Q exists; so is any call under VSA_COMPUTE_FP8 (the workspace
+ * holds E4M3). */
 int vsa_untile(const vsa_plan_t* plan, int which, const void* workspace, size_t ws_bytes,
                void* out, void* stream);
 

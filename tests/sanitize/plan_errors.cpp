@@ -143,6 +143,10 @@ static void check_valid(const char* name, const vsa_problem& p, const vsa_mask_p
   EXPECT(vsa_forward(plan, a, a, mis, a, a, ws, nullptr) == VSA_ERR_INVALID_ARG, "%s: misaligned v", name);
   EXPECT(vsa_forward_cached(plan, a, a, a, nullptr, a, ws, nullptr) == VSA_ERR_INVALID_ARG, "%s: cached NULL o", name);
   EXPECT(vsa_attend(plan, a, a, a, nullptr, a, ws, nullptr) == VSA_ERR_INVALID_ARG, "%s: attend NULL o", name);
+  if (m.compute == VSA_COMPUTE_BF16 && !(m.flags & VSA_FINE))
+    EXPECT(vsa_attend(plan, nullptr, a, a, a, a, ws, nullptr) == VSA_ERR_INVALID_ARG,
+           "%s: bf16 attend without q (read in raster order)", name);
+  EXPECT(vsa_untile(plan, 0, a, ws, a, nullptr) == VSA_ERR_UNSUPPORTED, "%s: untile of Q", name);
   EXPECT(vsa_layout(plan, a, nullptr, a, a, ws, nullptr) == VSA_ERR_INVALID_ARG, "%s: layout NULL k", name);
   EXPECT(vsa_untile(plan, 2, a, ws, a, nullptr) != VSA_OK, "%s: untile which = 2", name);
   int64_t kept = 0;

@@ -163,8 +163,12 @@ def test_fp8_workspace_regions():
         h = vsa.vsa_plan(prob, vsa.make_policy(vsa.VSA_WINDOW, win=(3, 3, 3), compute=compute))
         assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_EXP)[1] == want_exp
         assert vsa.vsa_workspace_region(h, _lib.VSA_WS_F8_AMAX)[1] == want_amax
-        # tile-major regions keep their bf16 size (E4M3 uses the first half)
-        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_QT)[1] == 6 * 8 * 32 * 128 * 2
+        # tile-major K keeps its bf16 size (E4M3 uses the first half); tile-major Q
+        # exists only for E4M3 (the bf16 attention reads Q in raster order)
+        want_q = 6 * 8 * 32 * 128 * 2 if compute == vsa.VSA_COMPUTE_FP8 else 0
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_QT)[1] == want_q
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_KT)[1] == 6 * 8 * 32 * 128 * 2
+        assert vsa.vsa_workspace_region(h, _lib.VSA_WS_VT)[1] == 6 * 8 * 32 * 128 * 2
 
 
 def test_exec_argument_errors_before_any_device_call():
