@@ -138,6 +138,20 @@ def _copy_gbs(dev, stage):
     return 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
+def _gemm_tflops(dev, stage):
+    """A dense bf16 GEMM (torch.matmul, 8192^3, random operands) in the same
+    run: what a library contraction with data-dependent operand toggling
+    reaches on this part, next to the datasheet peak."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    ms = stage(lambda: torch.matmul(a, b, out=c), 20)
+    del a, b, c
+    return 2.0 * 8192 ** 3 / (ms * 1e-3) / 1e12
+
+
 def _clamp_leg(wl, q, k, v, o, n, stage):
     """The same static workload with the window clamped at the grid edge
     (every window keeps its full 3x3x5 size: 13,500 tile pairs per head at
@@ -274,6 +288,7 @@ def main():
             and not wl.candidates and not f8 and not args.no_clamp_leg:
         clamp_leg = _clamp_leg(wl, q, k, v, o, n_st, stage)
     copy_gbs = None if wl.fine_group else _copy_gbs(dev, stage)
+    gemm_tflops = None if wl.fine_group or f8 else _gemm_tflops(dev, stage)
 
     choice = None
     if wl.candidates:  # heads per chosen blocking (SICS or profiling selector)
@@ -317,6 +332,8 @@ def main():
         "layout_copy_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / copy_gbs, 4)
                              if bytes_layout and copy_gbs else None),
         "attend_tflops": round(attn_tflops, 2),
+        "gemm_bf16_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
+        "attend_gemm_frac": round(attn_tflops / gemm_tflops, 4) if gemm_tflops else None,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "fp8": fp8_leg,

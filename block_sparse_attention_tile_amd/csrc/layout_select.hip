@@ -384,175 +384,302 @@ __global__ __launch_bounds__(kLayoutThreads) void untile_kernel(Geo g, const uin
 // Selection: one workgroup per (head, query tile).
 
 constexpr int kSelThreads = 256;
-constexpr int kSelBatch = 16;  // channels loaded per batch (d is a multiple of 16)
 constexpr int kMaxTiles = 4096;
 
 __device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
 }
 
+// One compare-exchange of the bitonic network for the element this thread
+// holds at sorted position x against its partner (so, io): the lower
+// position of an ascending block (x & kk == 0) keeps the element that ranks
+// first, every other position the one that ranks second.
+__device__ __forceinline__ void bitonic_keep(double& s, int& id, double so, int io, bool lower, bool up) {
+  const bool other_first = ranks_before(so, io, s, id);
+  if (other_first == (lower == up)) {
+    s = so;
+    id = io;
+  }
+}
+
+// In-register stage of stride JJ (< E): positions tid*E + r and tid*E + (r^JJ).
+template <int E, int JJ>
+__device__ __forceinline__ void bitonic_reg(double (&sv)[E], int (&si)[E], int kk) {
+  if constexpr (JJ < E) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      constexpr int dummy = 0;
+      (void)dummy;
+      const int pr = r ^ JJ;
+      if (pr > r) {
+        const bool up = (((int)threadIdx.x * E + r) & kk) == 0;
+        // r is the lower position of the pair
+        if (ranks_before(sv[pr], si[pr], sv[r], si[r]) == up) {
+          const double ts = sv[r];
+          sv[r] = sv[pr];
+          sv[pr] = ts;
+          const int ti = si[r];
+          si[r] = si[pr];
+          si[pr] = ti;
+        }
+      }
+    }
+  }
+}
+
+// Sort of m = 256 E (score, tile) pairs held E per thread in blocked order
+// (thread t holds positions t*E .. t*E + E - 1): highest score first, ties
+// by lower tile index.  Strides below E stay in registers, strides below
+// 64 E are lane shuffles inside a wave, the rest go through LDS (xs, xi).
+template <int E>
+__device__ void bitonic_sort_blocked(double (&sv)[E], int (&si)[E], double* xs, int* xi) {
+  const int tid = threadIdx.x;
+  constexpr int M = kSelThreads * E;
+  for (int kk = 2; kk <= M; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      if (jj < E) {
+        switch (jj) {
+          case 1: bitonic_reg<E, 1>(sv, si, kk); break;
+          case 2: bitonic_reg<E, 2>(sv, si, kk); break;
+          case 4: bitonic_reg<E, 4>(sv, si, kk); break;
+          default: bitonic_reg<E, 8>(sv, si, kk); break;
+        }
+      } else if (jj < 64 * E) {
+        const int dl = jj / E;  // lane distance of the partner
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const double so = __shfl_xor(sv[r], dl);
+          const int io = __shfl_xor(si[r], dl);
+          const int x = tid * E + r;
+          bitonic_keep(sv[r], si[r], so, io, (x & jj) == 0, (x & kk) == 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          xs[tid * E + r] = sv[r];
+          xi[tid * E + r] = si[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int x = tid * E + r;
+          bitonic_keep(sv[r], si[r], xs[x ^ jj], xi[x ^ jj], (x & jj) == 0, (x & kk) == 0);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// One workgroup per (head, QB consecutive query tiles): window and sink flags,
+// then the block scores of every key tile against each query tile (fixed-order
+// fp64 dot products of the summaries; one pass over the key summaries serves
+// all QB query tiles), held E per thread; for Top-K / Top-P each query tile's
+// row is sorted (bitonic, mostly in registers) and its first K positions, or
+// the shortest prefix whose softmax mass reaches p, are kept; the kept flags
+// are compacted in ascending order.
+template <int E, int QB>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float* __restrict__ pooled_q,
                                                              const float* __restrict__ pooled_k,
                                                              const float* __restrict__ pooled_kmin,
                                                              const int* __restrict__ cand,
                                                              int* __restrict__ row_len,
                                                              int* __restrict__ col_idx) {
-  __shared__ unsigned char keep[kMaxTiles];
-  __shared__ double sc[kMaxTiles];
-  __shared__ int sid[kMaxTiles];
-  __shared__ float qbar[128];
+  __shared__ unsigned char keep[QB][kMaxTiles];
+  __shared__ float qbar[QB][128];
   __shared__ int cnt[kSelThreads];
+  __shared__ double wsum[kSelThreads / 64];
+  __shared__ double top_s;
+  extern __shared__ __align__(16) unsigned char sel_dyn[];  // exchange: double [256 E], int [256 E]
+  double* const xs = reinterpret_cast<double*>(sel_dyn);
+  int* const xi = reinterpret_cast<int*>(xs + kSelThreads * E);
 
-  const int i = blockIdx.x;
+  const int i0 = blockIdx.x * QB;
   const long bh = blockIdx.y;
   const int c = cand_of(g, cand, bh);
   const BlkGeo b = pick_blk(g, c);
   const int n = b.n_tiles;
-  if (i >= n) return;
+  if (i0 >= n) return;
+  const int nq = min(QB, n - i0);  // query tiles of this workgroup
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int D = g.d;
   const bool dense = (g.flags & VSA_DENSE) != 0;
-  for (int j = tid; j < n; j += kSelThreads) keep[j] = (dense || j < g.sink) ? 1 : 0;
+  for (int x = tid; x < QB * n; x += kSelThreads) keep[x / n][x % n] = (dense || x % n < g.sink) ? 1 : 0;
   __syncthreads();
 
   if (g.flags & VSA_WINDOW) {
-    const int ci[3] = {i / (b.nt[1] * b.nt[2]), (i / b.nt[2]) % b.nt[1], i % b.nt[2]};
-    int lo[3], hi[3];
+    for (int qt = 0; qt < nq; ++qt) {
+      const int i = i0 + qt;
+      const int ci[3] = {i / (b.nt[1] * b.nt[2]), (i / b.nt[2]) % b.nt[1], i % b.nt[2]};
+      int lo[3], hi[3];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      const int r = (g.win[a] - 1) / 2;
-      const int nn = b.nt[a];
-      if (g.win_mode == VSA_WIN_CLAMP && nn >= 2 * r + 1) {
-        lo[a] = min(max(ci[a] - r, 0), nn - (2 * r + 1));
-        hi[a] = lo[a] + 2 * r;
-      } else {
-        lo[a] = max(ci[a] - r, 0);
-        hi[a] = min(ci[a] + r, nn - 1);
+      for (int a = 0; a < 3; ++a) {
+        const int r = (g.win[a] - 1) / 2;
+        const int nn = b.nt[a];
+        if (g.win_mode == VSA_WIN_CLAMP && nn >= 2 * r + 1) {
+          lo[a] = min(max(ci[a] - r, 0), nn - (2 * r + 1));
+          hi[a] = lo[a] + 2 * r;
+        } else {
+          lo[a] = max(ci[a] - r, 0);
+          hi[a] = min(ci[a] + r, nn - 1);
+        }
       }
-    }
-    const int e1 = hi[1] - lo[1] + 1, e2 = hi[2] - lo[2] + 1;
-    const int cells = (hi[0] - lo[0] + 1) * e1 * e2;
-    for (int x = tid; x < cells; x += kSelThreads) {
-      const int a0 = lo[0] + x / (e1 * e2);
-      const int a1 = lo[1] + (x / e2) % e1;
-      const int a2 = lo[2] + x % e2;
-      keep[(a0 * b.nt[1] + a1) * b.nt[2] + a2] = 1;
+      const int e1 = hi[1] - lo[1] + 1, e2 = hi[2] - lo[2] + 1;
+      const int cells = (hi[0] - lo[0] + 1) * e1 * e2;
+      for (int x = tid; x < cells; x += kSelThreads) {
+        const int a0 = lo[0] + x / (e1 * e2);
+        const int a1 = lo[1] + (x / e2) % e1;
+        const int a2 = lo[2] + x % e2;
+        keep[qt][(a0 * b.nt[1] + a1) * b.nt[2] + a2] = 1;
+      }
     }
   }
 
   const bool topp = (g.flags & VSA_TOPP) != 0;
   const int K = b.topk;
   if (topp || K > 0) {
-    for (int x = tid; x < D; x += kSelThreads) qbar[x] = pooled_q[(bh * g.max_tiles + i) * D + x];
+    for (int x = tid; x < QB * D; x += kSelThreads) {
+      const int qt = x / D, ch = x % D;
+      qbar[qt][ch] = qt < nq ? pooled_q[(bh * g.max_tiles + i0 + qt) * D + ch] : 0.f;
+    }
     __syncthreads();
-    int m = 1;
-    while (m < n) m <<= 1;
-    for (int j = tid; j < m; j += kSelThreads) {
-      if (j < n) {
-        // channel x of key tile j at [x][j]: consecutive lanes read consecutive words
-        const float* kr = pooled_k + bh * D * (long)g.max_tiles + j;
-        double acc = 0.0;
-        // Fixed left-to-right order; each fp32 x fp32 product is exact in
-        // fp64, so a fused multiply-add rounds exactly like mul-then-add.
-        if (g.summ == VSA_SUMM_MINMAX) {
-          const float* kn = pooled_kmin + bh * D * (long)g.max_tiles + j;
-          for (int x0 = 0; x0 < D; x0 += kSelBatch) {
-            float a[kSelBatch], c[kSelBatch];  // a batch of loads in flight, then the sums in order
+    // scores of key tiles j = tid * E + r (E consecutive tiles per thread:
+    // each channel's loads of a thread are contiguous) against the QB query tiles
+    const float* kr = pooled_k + bh * D * (long)g.max_tiles;
+    const float* kn = pooled_kmin + bh * D * (long)g.max_tiles;
+    double acc[QB][E];
 #pragma unroll
-            for (int u = 0; u < kSelBatch; ++u) {
-              a[u] = kr[(long)(x0 + u) * g.max_tiles];
-              c[u] = kn[(long)(x0 + u) * g.max_tiles];
+    for (int qt = 0; qt < QB; ++qt)
+#pragma unroll
+      for (int r = 0; r < E; ++r) acc[qt][r] = 0.0;
+    const int j0 = tid * E;
+    if (j0 < n) {
+      // channel x of key tile j at [x][j]; loads past the row re-read its last
+      // tile.  A batch of BT channels' loads is in flight before the sums,
+      // which run in the fixed channel order (each fp32 x fp32 product is
+      // exact in fp64).
+      constexpr int BT = E >= 8 ? 2 : 16 / E;
+      if (g.summ == VSA_SUMM_MINMAX) {
+        for (int x0 = 0; x0 < D; x0 += BT) {
+          float a[BT][E], cm[BT][E];
+#pragma unroll
+          for (int u = 0; u < BT; ++u)
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+              a[u][r] = kr[(long)(x0 + u) * g.max_tiles + min(j0 + r, n - 1)];
+              cm[u][r] = kn[(long)(x0 + u) * g.max_tiles + min(j0 + r, n - 1)];
             }
 #pragma unroll
-            for (int u = 0; u < kSelBatch; ++u)
-              acc += fmax((double)qbar[x0 + u] * (double)a[u], (double)qbar[x0 + u] * (double)c[u]);
-          }
-        } else {
-          for (int x0 = 0; x0 < D; x0 += kSelBatch) {
-            float a[kSelBatch];
+          for (int u = 0; u < BT; ++u)
 #pragma unroll
-            for (int u = 0; u < kSelBatch; ++u) a[u] = kr[(long)(x0 + u) * g.max_tiles];
+            for (int qt = 0; qt < QB; ++qt) {
+              const double qv = (double)qbar[qt][x0 + u];
 #pragma unroll
-            for (int u = 0; u < kSelBatch; ++u) acc = fma((double)qbar[x0 + u], (double)a[u], acc);
-          }
+              for (int r = 0; r < E; ++r) acc[qt][r] += fmax(qv * (double)a[u][r], qv * (double)cm[u][r]);
+            }
         }
-        sc[j] = acc * g.scale;
-        sid[j] = j;
       } else {
-        sc[j] = -DBL_MAX;
-        sid[j] = INT_MAX;
-      }
-    }
-    __syncthreads();
-    // Bitonic sort: highest score first, ties by lower tile index.
-    for (int kk = 2; kk <= m; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int x = tid; x < m; x += kSelThreads) {
-          const int y = x ^ jj;
-          if (y > x) {
-            const bool up = (x & kk) == 0;
-            const bool yfirst = ranks_before(sc[y], sid[y], sc[x], sid[x]);
-            if (yfirst == up) {
-              const double ts = sc[x];
-              sc[x] = sc[y];
-              sc[y] = ts;
-              const int ti = sid[x];
-              sid[x] = sid[y];
-              sid[y] = ti;
+        for (int x0 = 0; x0 < D; x0 += BT) {
+          float a[BT][E];
+#pragma unroll
+          for (int u = 0; u < BT; ++u)
+#pragma unroll
+            for (int r = 0; r < E; ++r) a[u][r] = kr[(long)(x0 + u) * g.max_tiles + min(j0 + r, n - 1)];
+#pragma unroll
+          for (int u = 0; u < BT; ++u)
+#pragma unroll
+            for (int qt = 0; qt < QB; ++qt) {
+              const double qv = (double)qbar[qt][x0 + u];
+#pragma unroll
+              for (int r = 0; r < E; ++r) acc[qt][r] = fma(qv, (double)a[u][r], acc[qt][r]);
             }
-          }
         }
-        __syncthreads();
       }
     }
-    for (int r = tid; r < K; r += kSelThreads) keep[sid[r]] = 1;
-    if (topp) {
-      // softmax weights of the sorted row, every thread its share of the
-      // exponentials (in place: the scores are not needed afterwards); then
-      // one thread sums them and walks the cumulative mass in sorted order
-      const double mx = sc[0];
-      __syncthreads();  // every thread has read sc[0]
-      for (int r = tid; r < n; r += kSelThreads) sc[r] = exp(sc[r] - mx);
-      __syncthreads();
-      if (tid == 0) {
-        double z = 0.0;
-        for (int r = 0; r < n; ++r) z += sc[r];
-        double cum = 0.0;
-        for (int r = 0; r < n; ++r) {
-          keep[sid[r]] = 1;
-          cum += sc[r] / z;
-          if (cum >= g.topp) break;
+#pragma unroll
+    for (int qt = 0; qt < QB; ++qt) {
+      if (qt >= nq) break;  // uniform
+      double sv[E];
+      int si[E];
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const bool valid = j0 + r < n;
+        sv[r] = valid ? acc[qt][r] * g.scale : -DBL_MAX;
+        si[r] = valid ? j0 + r : INT_MAX;
+      }
+      bitonic_sort_blocked<E>(sv, si, xs, xi);
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        if (tid * E + r < K) keep[qt][si[r]] = 1;
+      if (topp) {
+        // softmax weights in sorted order, their exclusive prefix sums (a
+        // fixed-order block scan), and the shortest prefix whose mass reaches
+        // p (the crossing tile included; every tile if the mass never does)
+        if (tid == 0) top_s = sv[0];
+        __syncthreads();
+        const double mx = top_s;
+        double e[E], loc = 0.0;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          e[r] = si[r] < n ? exp(sv[r] - mx) : 0.0;
+          loc += e[r];
         }
+        double inc = loc;  // inclusive scan inside the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double v = __shfl_up(inc, o);
+          if (lane >= o) inc += v;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        double before_wave = 0.0, z = 0.0;
+#pragma unroll
+        for (int w = 0; w < kSelThreads / 64; ++w) {
+          if (w < wave) before_wave += wsum[w];
+          z += wsum[w];
+        }
+        double before = before_wave + inc - loc;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (si[r] < n && before / z < g.topp) keep[qt][si[r]] = 1;
+          before += e[r];
+        }
+        __syncthreads();  // top_s and wsum are reused by the next query tile
       }
     }
   }
   __syncthreads();
 
-  // Ascending compaction of the kept flags.
+  // Ascending compaction of each query tile's kept flags.
   const int per = (n + kSelThreads - 1) / kSelThreads;
-  const int j0 = tid * per;
-  const int j1 = min(n, j0 + per);
-  int local = 0;
-  for (int j = j0; j < j1; ++j) local += keep[j];
-  cnt[tid] = local;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int x = 0; x < kSelThreads; ++x) {
-      const int v = cnt[x];
-      cnt[x] = run;
-      run += v;
+  const int c0 = tid * per;
+  const int c1 = min(n, c0 + per);
+  for (int qt = 0; qt < nq; ++qt) {
+    const int i = i0 + qt;
+    int local = 0;
+    for (int j = c0; j < c1; ++j) local += keep[qt][j];
+    cnt[tid] = local;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int x = 0; x < kSelThreads; ++x) {
+        const int v = cnt[x];
+        cnt[x] = run;
+        run += v;
+      }
+      row_len[bh * g.max_tiles + i] = min(run, g.row_cap);
     }
-    row_len[bh * g.max_tiles + i] = min(run, g.row_cap);
+    __syncthreads();
+    int pos = cnt[tid];
+    int* dst = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
+    for (int j = c0; j < c1; ++j)
+      if (keep[qt][j]) {
+        if (pos < g.row_cap) dst[pos] = j;
+        ++pos;
+      }
+    __syncthreads();  // cnt is reused by the next query tile
   }
-  __syncthreads();
-  int pos = cnt[tid];
-  int* dst = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
-  for (int j = j0; j < j1; ++j)
-    if (keep[j]) {
-      if (pos < g.row_cap) dst[pos] = j;
-      ++pos;
-    }
 }
 
 // Explicit instantiations of the layout kernels the launcher picks by value.
@@ -602,7 +729,22 @@ hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hi
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
   dim3 grid(g.max_tiles, g.B * g.H);
   const int* cand = per_head_blocking(g) ? w.cand : nullptr;
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, g, w.pooled_q, w.pooled_k, w.pooled_kmin, cand,
+  // elements per thread: the largest row, padded to a power of two >= 256
+  int m = kSelThreads;
+  while (m < g.max_tiles) m <<= 1;
+  const int E = m / kSelThreads;
+  const size_t dyn = (size_t)m * (sizeof(double) + sizeof(int));
+  // query tiles per workgroup: 4 while the row's scores fit in registers and
+  // the launch still has a few workgroups per SIMD (one pass over the key
+  // summaries then serves four rows: Wan-14B selection 1.43 -> 0.90 ms), else
+  // 1 (Wan-480p's 2,940 rows run faster one per workgroup)
+  const bool four = E <= 4 && (long)g.B * g.H * ((g.max_tiles + 3) / 4) >= 4096;
+  auto kern = four ? (E <= 1 ? select_kernel<1, 4> : E == 2 ? select_kernel<2, 4> : select_kernel<4, 4>)
+                   : (E <= 1 ? select_kernel<1, 1> : E == 2 ? select_kernel<2, 1> : E == 4 ? select_kernel<4, 1>
+                      : E == 8 ? select_kernel<8, 1> : select_kernel<16, 1>);
+  const int qb = four ? 4 : 1;
+  grid.x = (g.max_tiles + qb - 1) / qb;
+  hipLaunchKernelGGL(kern, grid, dim3(kSelThreads), dyn, s, g, w.pooled_q, w.pooled_k, w.pooled_kmin, cand,
                      w.row_len, w.col_idx);
   return hipGetLastError();
 }

@@ -62,32 +62,39 @@ __global__ __launch_bounds__(kAtomWaves * 64) void atom_kernel(Geo g, const uint
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
   int nz = 0;
-  for (int s0 = 0; s0 < n; s0 += TPW) {
-    const int s = s0 + grp;
-    float v[8];
+  constexpr int UP = 4;  // passes whose loads are in flight together
+  for (int s0 = 0; s0 < n; s0 += TPW * UP) {
+    uint4 raw[UP];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = 0.f;
-    if (s < n) {
-      const int st = s / (eh * ew), sh = (s / ew) % eh, sw = s % ew;
-      const long tok = ((long)(t0 + st) * g.grid[1] + (h0 + sh)) * g.grid[2] + (w0 + sw);
-      const uint4 raw = *reinterpret_cast<const uint4*>(x + tok * D + sub * 8);
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int u = 0; u < UP; ++u) {
+      const int s = s0 + u * TPW + grp;
+      raw[u] = make_uint4(0, 0, 0, 0);
+      if (s < n) {
+        const int st = s / (eh * ew), sh = (s / ew) % eh, sw = s % ew;
+        const long tok = ((long)(t0 + st) * g.grid[1] + (h0 + sh)) * g.grid[2] + (w0 + sw);
+        raw[u] = *reinterpret_cast<const uint4*>(x + tok * D + sub * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      float v[8];
+      const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         v[2 * c] = __uint_as_float(w4[c] << 16);
         v[2 * c + 1] = __uint_as_float(w4[c] & 0xffff0000u);
       }
-    }
-    float ss = 0.f;
+      float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) ss = fmaf(v[c], v[c], ss);
+      for (int c = 0; c < 8; ++c) ss = fmaf(v[c], v[c], ss);
 #pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) ss += __shfl_xor(ss, m);
-    if (ss > 0.f) {
-      const float inv = 1.0f / sqrtf(ss);
+      for (int m = 1; m < LPT; m <<= 1) ss += __shfl_xor(ss, m);
+      if (ss > 0.f) {  // a pass beyond the atom reads zeros: no contribution
+        const float inv = 1.0f / sqrtf(ss);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(v[c], inv, acc[c]);
-      nz += (sub == 0) ? 1 : 0;
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(v[c], inv, acc[c]);
+        nz += (sub == 0) ? 1 : 0;
+      }
     }
   }
   // reduce over the token groups of the wave
