@@ -49,6 +49,31 @@ hipError_t ensure_dyn_lds(const void* kernel, size_t bytes) {
   return e;
 }
 
+SideStreams* side_streams(hipStream_t caller, bool create) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  static std::mutex mu;
+  static SideStreams* made[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (made[dev] || !create) return made[dev];
+  // Streams are made outside stream capture only: a caller that captures
+  // before any uncaptured call on this device gets one stream.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  SideStreams* ss = new (std::nothrow) SideStreams();
+  if (!ss) return nullptr;
+  bool ok = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; ok && i < SideStreams::kN; ++i)
+    ok = hipStreamCreateWithFlags(&ss->s[i], hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&ss->join[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {  // partial set-up is kept out of use (and left allocated)
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  made[dev] = ss;
+  return ss;
+}
+
 }  // namespace vsa
 
 // Device scratch of vsa_forward_noalloc.  One copy of this array exists on
@@ -535,7 +560,7 @@ int enqueue_select(const vsa_plan_t* p, const void* q, const void* k, void* ws, 
 }
 
 int enqueue_attend(const vsa_plan_t* p, const void* q, const void* k, const void* v, void* o,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s, bool make_streams = true) {
   const Geo& g = p->geo;
   Ws w = resolve(p, ws);
   hipError_t e;
@@ -543,7 +568,7 @@ int enqueue_attend(const vsa_plan_t* p, const void* q, const void* k, const void
     e = vsa::launch_fine_attend(g, w, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                 (uint16_t*)o, s);
   else
-    e = vsa::launch_attend(g, w, (const uint16_t*)q, (uint16_t*)o, s);
+    e = vsa::launch_attend(g, w, (const uint16_t*)q, (uint16_t*)o, s, make_streams);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return VSA_OK;
 }
@@ -712,7 +737,9 @@ int vsa_forward_noalloc(const vsa_plan_t* p, const void* q, const void* k, const
   hipStream_t s = (hipStream_t)stream;
   if ((st = enqueue_layout(p, q, k, v, ws, s))) return st;
   if ((st = enqueue_select(p, q, k, ws, s))) return st;
-  if ((st = enqueue_attend(p, q, k, v, o, ws, s))) return st;
+  // Side streams are used if an earlier call on this device made them; this
+  // call makes none.
+  if ((st = enqueue_attend(p, q, k, v, o, ws, s, /*make_streams=*/false))) return st;
   return ok();
 }
 

@@ -686,20 +686,43 @@ hipError_t launch_d(const Geo& g, const Ws& w, int blocking, const int* cand, co
 
 }  // namespace
 
-hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s) {
+hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s,
+                         bool make_streams) {
   const int* cand = per_head_blocking(g) ? w.cand : nullptr;
-  // One launch per blocking (heads grouped by their chosen blocking); a
-  // workgroup whose head chose another blocking exits at once.
-  for (int c = 0; c < g.nb; ++c) {
-    hipError_t e;
+  auto one = [&](int c, hipStream_t st) -> hipError_t {
     if (g.f8)
-      e = (g.d == 128) ? launch_d<F8Core<128>>(g, w, c, cand, q, o, s) : launch_d<F8Core<64>>(g, w, c, cand, q, o, s);
-    else
-      e = (g.d == 128) ? launch_d<Bf16Core<128>>(g, w, c, cand, q, o, s)
-                       : launch_d<Bf16Core<64>>(g, w, c, cand, q, o, s);
-    if (e != hipSuccess) return e;
+      return (g.d == 128) ? launch_d<F8Core<128>>(g, w, c, cand, q, o, st)
+                          : launch_d<F8Core<64>>(g, w, c, cand, q, o, st);
+    return (g.d == 128) ? launch_d<Bf16Core<128>>(g, w, c, cand, q, o, st)
+                        : launch_d<Bf16Core<64>>(g, w, c, cand, q, o, st);
+  };
+  // One launch per blocking (heads grouped by their chosen blocking); a
+  // workgroup whose head chose another blocking exits at once.  The launches
+  // write disjoint heads, so blockings after the first go to side streams
+  // forked from and joined back into the caller's: the workgroups of a
+  // small-tile blocking (4 waves) then fill the CUs beside those of a
+  // large-tile one instead of waiting for them.
+  SideStreams* ss = g.nb > 1 ? side_streams(s, make_streams) : nullptr;
+  if (!ss) {
+    for (int c = 0; c < g.nb; ++c) {
+      const hipError_t e = one(c, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  return hipSuccess;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  hipError_t e = hipEventRecord(ss->fork, s);
+  int forked = 0;
+  for (; e == hipSuccess && forked < g.nb - 1; ++forked) e = hipStreamWaitEvent(ss->s[forked], ss->fork, 0);
+  for (int c = 0; e == hipSuccess && c < g.nb; ++c) e = one(c, c == 0 ? s : ss->s[c - 1]);
+  // Join every stream that was forked, also after an error, so that the
+  // caller's stream (or its capture) is never left with work outside it.
+  for (int i = 0; i < forked; ++i) {
+    hipError_t ej = hipEventRecord(ss->join[i], ss->s[i]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(s, ss->join[i], 0);
+    if (e == hipSuccess) e = ej;
+  }
+  return e;
 }
 
 }  // namespace vsa

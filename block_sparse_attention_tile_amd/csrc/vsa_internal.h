@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -119,6 +121,22 @@ constexpr size_t kNoAllocBytes = VSA_NOALLOC_BYTES;
 // device, once per (device, kernel); thread-safe (api.cpp).
 hipError_t ensure_dyn_lds(const void* kernel, size_t bytes);
 
+// Streams beside the caller's, one per blocking after the first, so that the
+// attention launches of different blockings (disjoint heads) can share the
+// CUs.  One set per device, made on first use; `mu` is held from the fork
+// event to the last join so that calls from several host threads do not mix
+// their events.  nullptr: none (not made yet and `create` false, the caller's
+// stream is being captured before the set exists, or creation failed); the
+// launches then run in order on the caller's stream.
+struct SideStreams {
+  static constexpr int kN = VSA_MAX_CAND - 1;
+  hipStream_t s[kN] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kN] = {};
+  std::mutex mu;
+};
+SideStreams* side_streams(hipStream_t caller, bool create);
+
 // Bytes of internal scratch the fine-grained mask needs (fine.hip).
 size_t fine_scratch_bytes(const Geo& g);
 
@@ -133,7 +151,8 @@ hipError_t launch_amax(const Geo& g, const Ws& w, const uint16_t* q, const uint1
 hipError_t launch_untile(const Geo& g, const Ws& w, int which, uint16_t* out, hipStream_t s);
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s);
 // (bf16 attention reads its query rows from the raster q)
-hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s);
+hipError_t launch_attend(const Geo& g, const Ws& w, const uint16_t* q, uint16_t* o, hipStream_t s,
+                         bool make_streams);
 hipError_t launch_sics(const Geo& g, const Ws& w, const uint16_t* q, const uint16_t* k,
                        hipStream_t s);
 // Profiling selector: per-head MSE of every candidate on the sampled rows,

@@ -17,7 +17,7 @@ hipError_t launch_amax(const Geo&, const Ws&, const uint16_t*, const uint16_t*, 
 }
 hipError_t launch_untile(const Geo&, const Ws&, int, uint16_t*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_select(const Geo&, const Ws&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_attend(const Geo&, const Ws&, const uint16_t*, uint16_t*, hipStream_t) {
+hipError_t launch_attend(const Geo&, const Ws&, const uint16_t*, uint16_t*, hipStream_t, bool) {
   return hipErrorNotSupported;
 }
 hipError_t launch_sics(const Geo&, const Ws&, const uint16_t*, const uint16_t*, hipStream_t) {
