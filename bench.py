@@ -26,9 +26,6 @@ METRIC = ("ms/attention call + effective TFLOP/s on retained blocks, "
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-ATTN_SOURCES = ["block_sparse_attention_tile_amd/csrc/attend.hip",
-                "block_sparse_attention_tile_amd/csrc/attn_core.h",
-                "block_sparse_attention_tile_amd/csrc/attn_core_f8.h"]
 
 
 def _src_hash(paths):
@@ -39,19 +36,114 @@ def _src_hash(paths):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = "block_sparse_attention_tile_amd/csrc"
+
+
+def _kernel_sources(name):
+    """The source files a kernel is built from: the csrc file that defines
+    its base name and every local header that file reaches."""
+    import re
+    base = re.match(r"(?:void\s+)?(?:\w+::)*(\w+)", name.strip()).group(1)
+    files = []
+    for f in sorted(os.listdir(os.path.join(ROOT, CSRC))):
+        if f.endswith(".hip") and re.search(r"void\s+%s\s*\(" % re.escape(base),
+                                             open(os.path.join(ROOT, CSRC, f)).read()):
+            files.append(f"{CSRC}/{f}")
+    if not files:
+        return base, None
+    todo, seen = list(files), []
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.append(f)
+        for inc in re.findall(r'^#include "([^"]+)"', open(os.path.join(ROOT, f)).read(), re.M):
+            todo.append(os.path.normpath(os.path.join(os.path.dirname(f), inc)))
+    return base, seen
+
+
+def _traffic(fragment, workload):
+    """HBM bytes per launch of the kernel whose name contains `fragment`,
+    from the committed rocprofv3 counter runs of `workload`; None when there
+    are none or the kernel's sources changed since they were taken."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        data = json.load(open(path))
-        ent = data[kernel_key][workload]
+        kernels = json.load(open(TRAFFIC_JSON))["workloads"][workload]["kernels"]
     except (KeyError, ValueError):
         return None
-    if ent.get("source_hash") != _src_hash(ATTN_SOURCES):
+    hits = [e for n, e in kernels.items() if fragment in n]
+    if len(hits) != 1 or hits[0].get("source_hash") != _src_hash(hits[0]["sources"]):
         return None
-    return ent.get("bytes_per_launch")
+    return hits[0]["bytes_per_launch"]
+
+
+def _short_name(name):
+    """A rocprofv3 kernel name without its parameter list, leading `void` or
+    anonymous namespaces: `vsa::attend_kernel<vsa::Bf16Core<128>, 12, 4, 1, false>`."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(", 1)[0].strip()
+
+
+def _counter_csv(path, counter):
+    """Per-dispatch values of one counter from a rocprofv3 counter_collection
+    csv: {kernel name: [value per dispatch]}."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (_short_name(r["Kernel_Name"]), r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), val in per.items():
+        out.setdefault(name, []).append(val)
+    return out
+
+
+def write_traffic(workload, fetch_csv, write_csv, command):
+    """Record HBM bytes per dispatch (medians) of every kernel of one
+    workload's counter runs in profiles/traffic.json.  The scale of each
+    counter comes from the largest plain device copy (`--copy-calib`, 1 GiB)
+    in the same run: bytes = counter KiB x 1024 / (counter KiB of the copy /
+    bytes the copy reads or writes)."""
+    import statistics
+    fetch, write = _counter_csv(fetch_csv, "FETCH_SIZE"), _counter_csv(write_csv, "WRITE_SIZE")
+    copy = "__amd_rocclr_copyBuffer"
+    if copy not in fetch or copy not in write:
+        raise SystemExit("no device copy in the counter runs: run bench.py with --copy-calib")
+    nbytes = 1 << 30
+    f_cal, w_cal = max(fetch[copy]), max(write[copy])
+    ff, wf = f_cal * 1024.0 / nbytes, w_cal * 1024.0 / nbytes
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    data.setdefault("workloads", {})
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        base, srcs = _kernel_sources(name)
+        if srcs is None:
+            continue  # not a kernel of this library (torch, the runtime's copies)
+        fk, wk = statistics.median(fetch[name]), statistics.median(write[name])
+        fb, wb = fk * 1024.0 / ff, wk * 1024.0 / wf
+        kernels[name] = {"base": base, "sources": srcs, "source_hash": _src_hash(srcs),
+                         "dispatches": len(fetch[name]), "fetch_kib_raw": fk, "write_kib_raw": wk,
+                         "fetch_bytes": round(fb), "write_bytes": round(wb),
+                         "bytes_per_launch": round(fb + wb)}
+    data["workloads"][workload] = {
+        "command": command,
+        "calibration": {"kernel": f"{copy}, device copy of 1 GiB", "bytes": nbytes,
+                        "FETCH_SIZE_kib": f_cal, "WRITE_SIZE_kib": w_cal,
+                        "fetch_factor": ff, "write_factor": wf},
+        "kernels": kernels}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    for name, e in kernels.items():
+        print(f"{name[:90]:90s} x{e['dispatches']:3d}  read {e['fetch_bytes'] / 1e9:8.3f} GB"
+              f"  written {e['write_bytes'] / 1e9:8.3f} GB")
 
 
 def _oracle_rows(wl, qn, kn, mem):
@@ -190,7 +282,16 @@ def main():
                     help="skip the E4M3 (VSA_COMPUTE_FP8) measurement of the same workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: record the HBM bytes per dispatch of the config's kernels "
+                         "from two rocprofv3 counter_collection csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE, each a run of bench.py --copy-calib) in profiles/traffic.json")
+    ap.add_argument("--command", default="",
+                    help="with --write-traffic: the profiling command to record beside the numbers")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.config, args.write_traffic[0], args.write_traffic[1], args.command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU: every stage is independent per (batch, head), so N GPUs would each take H/N heads with no exchange; run with --gpus 1",
                           "n_gpus": args.gpus}))
@@ -275,7 +376,8 @@ def main():
     bytes_layout = 0.0 if wl.fine_group else BH * wl.N * wl.d * per_tok
     attn_tflops = flops / (ms_attend * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
-    traffic = _traffic("attend_fp8" if f8 else "attend", wl.name)
+    traffic = _traffic(("fine_attend_kernel" if wl.fine_group else
+                        "attend_kernel<vsa::F8Core" if f8 else "attend_kernel<vsa::Bf16Core"), wl.name)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                 "traffic": traffic}
@@ -360,7 +462,7 @@ def _fp8_leg(wl, q, k, v, o, n, stage, flops):
             "stages_ms": {"layout": round(ms_layout, 4), "attend": round(ms_attend, 4)},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                         "traffic": _traffic("attend_fp8", wl.name)}}
+                         "traffic": _traffic("attend_kernel<vsa::F8Core", wl.name)}}
 
 
 def _mask_desc(wl):
