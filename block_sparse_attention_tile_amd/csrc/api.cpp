@@ -310,6 +310,13 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
     return fail(VSA_ERR_INVALID_ARG, "the tile sink does not apply to VSA_FINE");
   g.summ = po->summarizer;
   g.sink = po->sink;
+  // Kept tiles chosen by score alone (no window) are scattered over the
+  // head: an XCD's L2 finds little to reuse between neighbouring query
+  // tiles, and what matters is that the Infinity Cache holds the K and V of
+  // the heads in flight.  Their attention then walks the heads in order
+  // across the whole GPU.  A window keeps each XCD on its own run of
+  // neighbouring query tiles instead.
+  g.head_sync = !(f & VSA_WINDOW) && (f & (VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)) ? 1 : 0;
   if (po->compute != VSA_COMPUTE_BF16 && po->compute != VSA_COMPUTE_FP8)
     return fail(VSA_ERR_INVALID_ARG, "compute must be VSA_COMPUTE_BF16 or VSA_COMPUTE_FP8 (got %d)",
                 po->compute);
@@ -641,6 +648,7 @@ int vsa_plan_get_info(const vsa_plan_t* p, vsa_plan_info* info) {
   }
   info->max_tiles = g.max_tiles;
   info->row_cap = g.row_cap;
+  info->head_sync = g.head_sync;
   info->static_pairs = p->static_pairs;
   info->static_flops = p->static_flops;
   info->fine_groups = g.fine_G;
@@ -840,6 +848,7 @@ int vsa_retained_work(const vsa_plan_t* p, const void* ws, size_t ws_bytes, int6
       for (int gi = 0; gi < g.fine_G; ++gi) {
         long rowsg = std::min<long>(g.fine_M, (long)g.N - (long)gi * g.fine_M);
         long c = cnt[bh * g.fine_G + gi];
+        if (c < 0 || c > g.N) return fail(VSA_ERR_HIP, "corrupt fine count %ld for head %ld", c, bh);
         pr += c;
         fl += 4.0 * g.d * (double)rowsg * (double)c;
       }

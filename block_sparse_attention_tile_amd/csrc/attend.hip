@@ -110,6 +110,26 @@ constexpr int kFlagShift = 2 * kTileBits;
 constexpr int kUnitNvShift = kTileBits + 8;  // unit-table entries: valid keys of the unit, minus 1
 __device__ __forceinline__ int entry_nv(int x) { return (x >> kTileBits) & ((1 << kTileBits) - 1); }
 
+// The r-th head, in head order, whose chosen blocking is `blocking` (every
+// head without a per-head choice); -1 past the last.  Wave-uniform: each
+// lane tests one head of a 64-head window, a ballot counts the hits.
+__device__ __forceinline__ long nth_head(const Geo& g, const int* cand, int blocking, int r) {
+  const long BH = (long)g.B * g.H;
+  if (!cand) return r < BH ? r : -1;
+  const int lane = threadIdx.x & 63;
+  for (long base = 0; base < BH; base += 64) {
+    const long h = base + lane;
+    const uint64_t hits = __ballot(h < BH && cand_of(g, cand, h) == blocking);
+    const int n = __popcll(hits);
+    if (r < n) {
+      const bool mine = ((hits >> lane) & 1) && __popcll(hits & ((1ull << lane) - 1)) == r;
+      return base + __ffsll((unsigned long long)__ballot(mine)) - 1;
+    }
+    r -= n;
+  }
+  return -1;
+}
+
 // Iterator over the 64-key chunks of a query tile's kept key tiles.
 struct ChunkIter {
   int e;    // position in the kept list
@@ -326,16 +346,36 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
   constexpr int KU = C::kF8 ? 32 : 16;  // keys per unit (unit mode)
   constexpr int UPC = kKC / KU;         // units per chunk
 
-  // XCD-major mapping of workgroups to work items.
-  const int units = (g.max_tiles + TPW - 1) / TPW;  // tiles (or pairs) per head
-  const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
-  const int item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
-  if (item >= n_items) return;
-  const int sb = item % nsb;
-  const int i0 = ((item / nsb) % units) * TPW;  // first query tile of the workgroup
-  const long bh = item / (nsb * units);
-  if (cand_of(g, cand, bh) != blocking) return;
+  // Workgroups to work items (head, query tile or pair, slab group).  The
+  // hardware deals consecutive workgroups to the eight XCDs in turn.
   const BlkGeo b = pick_blk(g, blocking);
+  int sb, i0;
+  long bh;
+  if (g.head_sync) {
+    // Head-synchronous: every XCD takes one contiguous eighth of each head's
+    // items, and all XCDs walk the heads that chose this blocking in order.
+    const int per_head = (b.n_tiles + TPW - 1) / TPW * nsb;
+    const int per_hx = (per_head + kNumXcd - 1) / kNumXcd;
+    const int j = blockIdx.x / kNumXcd;
+    const int in_head = (blockIdx.x % kNumXcd) * per_hx + j % per_hx;
+    if (in_head >= per_head) return;
+    bh = nth_head(g, cand, blocking, j / per_hx);
+    if (bh < 0) return;
+    sb = in_head % nsb;
+    i0 = in_head / nsb * TPW;
+  } else {
+    // XCD-major: each XCD takes one contiguous range of all items, so
+    // neighbouring query tiles of a head (sharing window tiles) run on the
+    // same XCD and its L2.
+    const int units = (g.max_tiles + TPW - 1) / TPW;  // tiles (or pairs) per head
+    const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
+    const int item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    if (item >= n_items) return;
+    sb = item % nsb;
+    i0 = ((item / nsb) % units) * TPW;  // first query tile of the workgroup
+    bh = item / (nsb * units);
+    if (cand_of(g, cand, bh) != blocking) return;
+  }
   if (i0 >= b.n_tiles) return;
   const int slots = b.slots;
   const int q0 = sb * WPT * 32;
@@ -620,9 +660,16 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
   const BlkGeo& b = g.blk[blocking];
   const int slabs = b.slots / 32;
   const int nsb = (slabs + NW / TPW - 1) / (NW / TPW);
-  const long units = (g.max_tiles + TPW - 1) / TPW;
-  const long items = (long)g.B * g.H * units * nsb;
-  const int per_xcd = (int)((items + kNumXcd - 1) / kNumXcd);
+  const long BH = (long)g.B * g.H;
+  long items, per_xcd;
+  if (g.head_sync) {  // every head's items in eight contiguous ranges (see the kernel)
+    const long per_head = (b.n_tiles + TPW - 1) / TPW * (long)nsb;
+    items = BH * per_head;
+    per_xcd = (per_head + kNumXcd - 1) / kNumXcd * BH;
+  } else {
+    items = BH * ((g.max_tiles + TPW - 1) / TPW) * nsb;
+    per_xcd = (items + kNumXcd - 1) / kNumXcd;
+  }
   const size_t shmem = attend_shmem<C, STAGES, TPW, UN>(g, blocking);
   // more than 64 KB of dynamic LDS must be requested (per device)
   hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(&attend_kernel<C, NW, STAGES, TPW, UN>), shmem);

@@ -38,6 +38,7 @@ struct Geo {
   double scale;     // softmax scale
   int summ;         // VSA_SUMM_* (dynamic masks)
   int sink;         // leading key tiles kept for every query tile
+  int head_sync;    // attention: head-synchronous workgroup order (masks without a window)
   int f8;           // 1 under VSA_COMPUTE_FP8: E4M3 tile-major Q, K, V and attention
   int prof_runs;    // VSA_PROFILE_SELECT: sampled runs of 32 query rows per head
   int prof_segs;    // key segments (ranges of raster lines) of the full pass

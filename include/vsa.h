@@ -191,6 +191,14 @@ typedef struct vsa_plan_info {
                                      multiples of 64, ragged edge tiles), unless the
                                      unit table does not fit in LDS at launch; 0
                                      without pairing */
+  int32_t head_sync;              /* 1: attention workgroups are ordered head by head
+                                     across the whole GPU (each XCD takes one contiguous
+                                     range of every head's query tiles): masks without a
+                                     window, whose kept tiles have no spatial locality for
+                                     an XCD's L2 to use, then keep only a head or two of
+                                     K and V in the Infinity Cache at a time. 0: each XCD
+                                     takes one contiguous range of all (head, tile)
+                                     items, which keeps neighbouring windows together */
 } vsa_plan_info;
 
 /* Workspace regions, for inspection by tests (see vsa_workspace_region). */

@@ -118,3 +118,11 @@ def test_cached_on_unwritten_selection_gives_zeros(name):
     plan.forward_cached(q, k, v, o)
     torch.cuda.synchronize()
     assert torch.count_nonzero(o).item() == 0
+    # the host-side getters refuse the poisoned fields instead of indexing with them
+    # (blocking index -1 under SICS, row length -1 otherwise)
+    if name != "fine":
+        with pytest.raises(vsa.VsaError, match="corrupt blocking index" if name == "sics" else "corrupt row length"):
+            plan.read_selection()
+    with pytest.raises(vsa.VsaError, match="corrupt"):
+        plan.retained_work()
+

@@ -26,6 +26,11 @@ SMALL = {
     "sics_ragged_d64": Workload("sics_ragged_d64", 2, 2, 64, (7, 20, 16), (1, 16, 16),
                                 candidates=((1, 16, 16), (7, 4, 4)), topk_frac=0.25,
                                 window=(1, 1, 3), ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0)),
+    # 72 heads: the head-synchronous attention order finds the r-th head of a
+    # blocking across two 64-head ballot windows
+    "sics_72_heads": Workload("sics_72_heads", 2, 36, 64, (7, 16, 16), (1, 16, 16),
+                              candidates=((1, 16, 16), (7, 4, 4)), topk_frac=0.25,
+                              ell=(8.0, 1.0, 1.0), ell_alt=(1.0, 8.0, 8.0)),
 }
 
 
@@ -61,6 +66,8 @@ def test_sics_choice_selection_attention(name):
     q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=1, device="cuda")
     prob, pol = structs_of(wl)
     plan = vsa.Plan(prob, pol)
+    # Top-K without a window: attention workgroups ordered head by head
+    assert plan.info.head_sync == (wl.window is None)
     o = plan.forward(q, k, v)
     torch.cuda.synchronize()
     nb = len(wl.candidates)

@@ -146,6 +146,8 @@ def test_selection_and_attention_small(name):
     plan, o = _run_all(wl, q, k, v)
     if name in KERNELS:  # (pair, units)
         assert (plan.info.pair[0], plan.info.units[0]) == KERNELS[name]
+    # score-only masks (no window) order the attention head by head
+    assert plan.info.head_sync == int(wl.window is None and bool(wl.topk or wl.topk_frac or wl.topp))
     row_ptr, col, _ = plan.read_selection()
     qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
     on = o.float().cpu().numpy()
