@@ -75,7 +75,8 @@ class vsa_plan_info(C.Structure):
                 ("static_flops", C.c_double), ("fine_groups", C.c_int32),
                 ("fine_keep_count", C.c_int64), ("fine_cap", C.c_int64), ("scale", C.c_double),
                 ("pair", C.c_int32 * VSA_MAX_CAND),
-                ("units", C.c_int32 * VSA_MAX_CAND), ("head_sync", C.c_int32)]
+                ("units", C.c_int32 * VSA_MAX_CAND),
+                ("interleave", C.c_int32 * VSA_MAX_CAND), ("head_sync", C.c_int32)]
 
 
 class VsaError(RuntimeError):

@@ -147,15 +147,20 @@ void static_row(const Geo& g, const BlkGeo& b, int i, std::vector<char>& keep) {
 // blocking in one workgroup that streams the union of their kept lists.
 // Only groups of 4 to 6 waves (tiles of 97..192 slots) are paired, giving
 // 8- to 12-wave workgroups with a 4-stage ring.  Top-P rows keep most tiles
-// and neighbours' rows nearly coincide; Top-K rows of neighbours overlap far
-// less, so they are not paired; static masks are paired when the pairs'
-// lists overlap enough that at least 70% of the staged chunks serve both
-// tiles' waves.
+// and neighbours' rows nearly coincide.  Top-K rows of neighbours share only
+// about half their tiles: tiles of 6 slabs are paired with the interleaved
+// schedule (interleaved_pairs), which stages each shared tile once and keeps
+// both halves busy on the rest (Wan-14B shape, 3x8x8 tiles: 29.5 -> 27.4 ms);
+// tiles of 4 slabs are not (7x4x4 tiles: 37.2 -> 41.2 ms, though the
+// traffic from beyond L2 fell by 15%: two independent four-wave workgroups
+// per CU hide load latency better than one eight-wave workgroup).  Static
+// masks are paired when the pairs' lists overlap enough that at least 70% of
+// the staged chunks serve both tiles' waves.
 int pair_tiles(const Geo& g, const BlkGeo& b) {
   const int slabs = b.slots / 32;
   if (slabs < 4 || slabs > 6) return 0;
   if (g.flags & VSA_TOPP) return 1;
-  if (g.flags & (VSA_TOPK | VSA_TOPK_FRAC)) return 0;
+  if (g.flags & (VSA_TOPK | VSA_TOPK_FRAC)) return slabs == 6 ? 1 : 0;
   std::vector<char> ka(b.n_tiles), kb(b.n_tiles);
   double used = 0.0, staged = 0.0;
   for (int i = 0; i < b.n_tiles; i += 2) {
@@ -196,7 +201,7 @@ long tile_valid_id(const Geo& g, const BlkGeo& b, int i) {
 // (One-tile workgroups stay with whole chunks: bf16 units measured no faster
 // there, on 112-, 208- and 480-key tiles.)
 int unit_tiles(const Geo& g, const BlkGeo& b) {
-  if (!b.pair) return 0;
+  if (!b.pair || vsa::interleaved_pairs(g)) return 0;  // the interleaved schedule works on whole chunks
   const long ku = g.f8 ? 32 : 16;
   long units = 0, chunks = 0;
   for (int i = 0; i < b.n_tiles; ++i) {
@@ -645,6 +650,7 @@ int vsa_plan_get_info(const vsa_plan_t* p, vsa_plan_info* info) {
     info->topk[c] = g.blk[c].topk;
     info->pair[c] = g.blk[c].pair;
     info->units[c] = g.blk[c].units;
+    info->interleave[c] = g.blk[c].pair && !g.blk[c].units && vsa::interleaved_pairs(g) ? 1 : 0;
   }
   info->max_tiles = g.max_tiles;
   info->row_cap = g.row_cap;

@@ -161,6 +161,36 @@ struct ChunkIter {
   __device__ __forceinline__ int keys() const { return min(kKC, nv - off); }
 };
 
+// Interleaved pair schedule (interleaved_pairs): one entry per chunk, with
+// the key tile in the low kTileBits bits, the chunk's index inside the tile
+// in the next 4, its valid keys minus one from bit kCkKeysShift (6 bits)
+// and the query-tile flags from kFlagShift.
+constexpr int kCkKeysShift = kTileBits + 4;
+
+struct ListIter {
+  int c;    // position in the schedule
+  int j;    // key tile
+  int off;  // first slot of the chunk inside tile j
+  int kv;   // valid keys of the chunk
+  int fl;   // query tiles of the workgroup that keep tile j
+  __device__ __forceinline__ void load(const int* ck) {
+    const int x = __builtin_amdgcn_readfirstlane(ck[c]);  // uniform: keep the iterator scalar
+    j = x & ((1 << kTileBits) - 1);
+    off = ((x >> kTileBits) & 15) * kKC;
+    kv = ((x >> kCkKeysShift) & 63) + 1;
+    fl = x >> kFlagShift;
+  }
+  __device__ __forceinline__ void start(const int* ck, int n) {
+    c = 0;
+    j = off = kv = fl = 0;
+    if (n > 0) load(ck);
+  }
+  __device__ __forceinline__ void next(const int* ck, int n) {
+    if (++c < n) load(ck);
+  }
+  __device__ __forceinline__ int keys() const { return kv; }
+};
+
 // Unit mode: element offsets of the first key of a chunk's four 16-key
 // units in the head's K (k0..k3) and V^T (v0..v3).
 struct UnitBases {
@@ -430,6 +460,36 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
         cols[n++] = (fl << kFlagShift) | (tile_nvalid(g, b, j) << kTileBits) | j;
       }
       *nu = n;
+      if constexpr (!UN) {
+        if (interleaved_pairs(g)) {
+          // the chunks both tiles keep (ascending), then the chunks only one
+          // keeps, taken from the two tiles' ascending lists in turn
+          int* ck = cols + ((4 * g.row_cap + 2 + 3) & ~3);
+          int m = 0;
+          auto emit = [&](int x, int off) {
+            ck[m++] = (x & ((1 << kTileBits) - 1)) | ((off / kKC) << kTileBits) |
+                      ((min(kKC, entry_nv(x) - off) - 1) << kCkKeysShift) | ((x >> kFlagShift) << kFlagShift);
+          };
+          for (int e = 0; e < n; ++e)
+            if ((cols[e] >> kFlagShift) == 3)
+              for (int off = 0; off < entry_nv(cols[e]); off += kKC) emit(cols[e], off);
+          auto next_of = [&](int e, int f) {
+            do ++e; while (e < n && ((cols[e] >> kFlagShift) != f || entry_nv(cols[e]) == 0));
+            return e;
+          };
+          int ea = next_of(-1, 1), eb = next_of(-1, 2), oa = 0, ob = 0;
+          while (ea < n || eb < n) {
+            if (ea < n) {
+              emit(cols[ea], oa);
+              if ((oa += kKC) >= entry_nv(cols[ea])) { oa = 0; ea = next_of(ea, 1); }
+            }
+            if (eb < n) {
+              emit(cols[eb], ob);
+              if ((ob += kKC) >= entry_nv(cols[eb])) { ob = 0; eb = next_of(eb, 2); }
+            }
+          }
+        }
+      }
       if constexpr (UN) {
         // first unit of each union entry (la, lb are free now), total units
         // (ascending tile order: a 32-key block that mixes tiles kept by one
@@ -560,37 +620,51 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
       }
     }
   } else {
-    ChunkIter ld_it, cur;
-    ld_it.start(cols, L);
-    cur = ld_it;
+    // one chunk sequence: the kept list (or the pair's union) chunk by
+    // chunk, or the interleaved pair schedule (same chunks, other order)
+    auto stream = [&](auto ld_it, const int* lst, int nl) {
+      auto cur = ld_it;
 #pragma unroll
-    for (int s = 0; s < CPB; ++s) {
-      if (s < total) {
-        ldr.issue(lds + s * Stage::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
-                  vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-        ld_it.next(cols, L);
-      }
-    }
-    for (int c = 0; c < total; c += CPB) {
-      wait_loads_and_barrier();
-#pragma unroll
-      for (int u = 0; u < CPB; ++u) {
-        const int nc = c + CPB + u;
-        if (nc < total) {
-          ldr.issue(lds + (nc % STAGES) * Stage::STAGE,
-                    kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+      for (int s = 0; s < CPB; ++s) {
+        if (s < total) {
+          ldr.issue(lds + s * Stage::STAGE, kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
                     vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
-          ld_it.next(cols, L);
+          ld_it.next(lst, nl);
         }
       }
+      for (int c = 0; c < total; c += CPB) {
+        wait_loads_and_barrier();
 #pragma unroll
-      for (int u = 0; u < CPB; ++u) {
-        if (c + u < total) {
-          const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
-          if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
-          cur.next(cols, L);
+        for (int u = 0; u < CPB; ++u) {
+          const int nc = c + CPB + u;
+          if (nc < total) {
+            ldr.issue(lds + (nc % STAGES) * Stage::STAGE,
+                      kt_head + ((long)ld_it.j * slots + ld_it.off) * D,
+                      vt_head + (long)ld_it.j * D * slots + ld_it.off, ld_it.keys() <= 32);
+            ld_it.next(lst, nl);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CPB; ++u) {
+          if (c + u < total) {
+            const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
+            if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+            cur.next(lst, nl);
+          }
         }
       }
+    };
+    bool ilv = false;
+    if constexpr (TPW == 2) ilv = interleaved_pairs(g);
+    if (ilv) {
+      const int* ck = cols + ((4 * g.row_cap + 2 + 3) & ~3);
+      ListIter it;
+      it.start(ck, total);
+      stream(it, ck, total);
+    } else {
+      ChunkIter it;
+      it.start(cols, L);
+      stream(it, cols, L);
     }
   }
 
@@ -641,10 +715,16 @@ VSA_ATTEND_INST_UN(F8Core<64>)
 // Dynamic LDS of a launch: the K/V ring, then the kept list (TPW = 1) or the
 // union (up to twice a row), both tiles' lists and the union's length; in
 // unit mode also the total units and the unit table (the union's entries
-// times the units of a full tile, padded to whole chunks).
+// times the units of a full tile, padded to whole chunks); for interleaved
+// pairs the schedule (the union's entries times the chunks of a full tile).
 template <class C, int STAGES, int TPW, bool UN = false>
 size_t attend_shmem(const Geo& g, int blocking) {
   size_t list_ints = TPW == 1 ? (size_t)g.row_cap : 4 * (size_t)g.row_cap + 1;
+  if (TPW == 2 && !UN && interleaved_pairs(g)) {  // + the interleaved schedule: the union's chunks
+    const size_t entries = std::min<size_t>(2 * (size_t)g.row_cap, (size_t)g.blk[blocking].n_tiles);
+    list_ints = ((4 * (size_t)g.row_cap + 2 + 3) & ~(size_t)3) +
+                entries * (size_t)((g.blk[blocking].slots + kKC - 1) / kKC);
+  }
   if (UN) {
     const size_t entries = std::min<size_t>(2 * (size_t)g.row_cap, (size_t)g.blk[blocking].n_tiles);
     list_ints = ((4 * (size_t)g.row_cap + 2 + 3) & ~(size_t)3) +

@@ -66,6 +66,15 @@ __host__ __device__ __forceinline__ bool per_head_blocking(const Geo& g) {
 // The blocking chosen for head bh (0 without a per-head choice), clamped to a
 // valid index, so that a workspace whose selection was never written (a
 // cached call on a fresh workspace) still addresses memory in bounds.
+// Whether paired query tiles (whole-chunk mode) stream an interleaved chunk
+// schedule instead of their ascending union: the chunks both tiles keep,
+// then the chunks only one keeps, the two tiles' alternating, so that in
+// each step of two chunks both halves of the workgroup have work.  Used for
+// Top-K masks, whose neighbouring rows share only about half their tiles.
+__host__ __device__ __forceinline__ bool interleaved_pairs(const Geo& g) {
+  return (g.flags & (VSA_TOPK | VSA_TOPK_FRAC)) != 0 && (g.flags & VSA_TOPP) == 0;
+}
+
 __device__ __forceinline__ int cand_of(const Geo& g, const int* cand, long bh) {
   return cand ? min(max(cand[bh], 0), g.nb - 1) : 0;
 }

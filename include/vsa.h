@@ -191,6 +191,11 @@ typedef struct vsa_plan_info {
                                      multiples of 64, ragged edge tiles), unless the
                                      unit table does not fit in LDS at launch; 0
                                      without pairing */
+  int32_t interleave[VSA_MAX_CAND];/* 1: this paired blocking (Top-K masks) streams an
+                                     interleaved schedule instead of the ascending union:
+                                     the chunks both tiles keep, then the chunks only one
+                                     keeps, alternating between the two tiles, so both
+                                     halves of the workgroup compute in every step */
   int32_t head_sync;              /* 1: attention workgroups are ordered head by head
                                      across the whole GPU (each XCD takes one contiguous
                                      range of every head's query tiles): masks without a

@@ -230,8 +230,9 @@ def test_profile_errors_and_sizes():
 
 def test_attention_pairs_query_tiles_where_lists_overlap():
     """Plan-time choice of two query tiles per attention workgroup: tiles of 4 to 6 slabs
-    under Top-P, or under a static mask whose neighbours' lists mostly coincide; never for
-    Top-K, a 1x1x1 window or larger tiles."""
+    under Top-P, or under a static mask whose neighbours' lists mostly coincide; under Top-K
+    only tiles of 6 slabs, with the interleaved schedule; never for a 1x1x1 window or larger
+    tiles."""
     from synth import CONFIGS, Workload
     from block_sparse_attention_tile_amd.workload import plan_structs
 
@@ -243,7 +244,10 @@ def test_attention_pairs_query_tiles_where_lists_overlap():
     assert pair(Workload("w", 1, 2, 128, (6, 12, 40), (3, 6, 8), window=(1, 1, 1))) == [0]
     assert pair(Workload("k", 1, 2, 128, (7, 8, 8), (7, 4, 4), topk=3)) == [0]
     assert pair(CONFIGS["hunyuan"]) == [0]
-    assert pair(CONFIGS["wan14b"]) == [0, 0, 0]
+    assert pair(CONFIGS["wan14b"]) == [0, 0, 1]  # 256-, 112- and 192-token tiles
+    p = vsa.Plan(*plan_structs(CONFIGS["wan14b"]))
+    assert list(p.info.interleave)[:3] == [0, 0, 1] and list(p.info.units)[:3] == [0, 0, 0]
+    assert list(vsa.Plan(*plan_structs(CONFIGS["wan480"])).info.interleave)[:1] == [0]  # Top-P: union
 
 
 def test_attention_units_where_tails_are_short():

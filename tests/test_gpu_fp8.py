@@ -68,6 +68,8 @@ CASES = {
     # paired 156-token tiles at d = 64: 32-key units (five per tile, the last with 28 keys),
     # 12-token edge tiles
     "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 13), topp=0.8, compute="fp8"),
+    # Top-K pairs of 192-token tiles (interleaved schedule), ragged, odd tile count
+    "topk_pair_ragged": Workload("topk_pair_ragged", 1, 3, 64, (7, 8, 20), (3, 8, 8), topk=4, compute="fp8"),
 }
 
 
@@ -192,7 +194,7 @@ def test_fp8_layout_codes_bit_exact(name):
 
 
 # cases that exist to run the paired / unit kernels: the plan must choose them
-PAIRED_UNITS = {"w480_mini": (1, 1), "pair_units_d64": (1, 1)}
+PAIRED_UNITS = {"w480_mini": (1, 1), "pair_units_d64": (1, 1), "topk_pair_ragged": (1, 0)}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -203,6 +205,7 @@ def test_fp8_attention_small(name):
     plan = vsa.Plan(*structs_of(wl))
     if name in PAIRED_UNITS:
         assert (plan.info.pair[0], plan.info.units[0]) == PAIRED_UNITS[name]
+    assert plan.info.interleave[0] == int(name == "topk_pair_ragged")
     o = plan.forward(q, k, v)
     torch.cuda.synchronize()
     row_ptr, col, cand = plan.read_selection()

@@ -58,6 +58,10 @@ SMALL = {
     "topk_96": Workload("topk_96", 2, 2, 64, (6, 8, 24), (2, 4, 12), window=(3, 1, 1), topk=2),
     # 336-token tiles (eleven-wave workgroups, 4-stage ring, a 16-key tail chunk per tile),
     # static window, ragged H
+    # Top-K over 192-token tiles: query tiles paired, interleaved schedule
+    "topk_pair_192": Workload("topk_pair_192", 1, 2, 128, (6, 16, 24), (3, 8, 8), topk=3),
+    # the same with ragged edge tiles, an odd tile count (the last pair has one tile) and d=64
+    "topk_pair_ragged": Workload("topk_pair_ragged", 1, 3, 64, (7, 8, 20), (3, 8, 8), topk=4),
     "eleven_slab_units": Workload("eleven_slab_units", 1, 2, 128, (12, 13, 24), (6, 7, 8), window=(3, 3, 3)),
 }
 
@@ -135,7 +139,10 @@ def test_pooled_means_bit_exact(name):
 # (pair, units) the plan must choose for the cases that exist to run the
 # paired / unit kernels (and for two that must not)
 KERNELS = {"w480_mini": (1, 1), "pair_window_odd": (1, 1), "pair_units_105": (1, 1),
-           "pair_units_d64": (1, 1), "eleven_slab_units": (0, 0), "hy_mini": (0, 0)}
+           "pair_units_d64": (1, 1), "eleven_slab_units": (0, 0), "hy_mini": (0, 0),
+           "topk_only": (0, 0), "topk_max": (0, 0), "topk_pair_192": (1, 0), "topk_pair_ragged": (1, 0)}
+# Top-K pairs (six-slab tiles) stream the interleaved schedule
+INTERLEAVED = {"topk_pair_192", "topk_pair_ragged"}
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -146,6 +153,7 @@ def test_selection_and_attention_small(name):
     plan, o = _run_all(wl, q, k, v)
     if name in KERNELS:  # (pair, units)
         assert (plan.info.pair[0], plan.info.units[0]) == KERNELS[name]
+    assert plan.info.interleave[0] == int(name in INTERLEAVED), list(plan.info.interleave)
     # score-only masks (no window) order the attention head by head
     assert plan.info.head_sync == int(wl.window is None and bool(wl.topk or wl.topk_frac or wl.topp))
     row_ptr, col, _ = plan.read_selection()
