@@ -62,7 +62,6 @@ struct F8Core {
 };
 
 constexpr int kMaxWaves = 12;
-constexpr int kNumXcd = 8;
 
 struct TileInfo {
   int it, ih, iw, et, eh, ew, nvalid;

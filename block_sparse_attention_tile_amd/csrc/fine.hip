@@ -874,8 +874,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fine_attend_kernel(Geo g, const ui
                                                               const int* __restrict__ idx,
                                                               uint16_t* __restrict__ o) {
   extern __shared__ __align__(16) uint16_t lds[];
-  const int gi = blockIdx.x;
-  const long bh = blockIdx.y;
+  // XCD-major: the hardware deals consecutive workgroups to the eight XCDs
+  // in turn; each XCD takes one contiguous range of (head, group) items, so
+  // neighbouring groups, whose kept keys overlap (about half of them for
+  // adjacent groups of smooth inputs), gather through the same L2
+  const long n_items = (long)g.B * g.H * g.fine_G;
+  const long per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
+  const long item = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+  if (item >= n_items) return;
+  const int gi = (int)(item % g.fine_G);
+  const long bh = item / g.fine_G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hi = lane >> 5;
   const int row0 = gi * g.fine_M + wave * 32;                 // first query row of this wave
@@ -936,7 +944,9 @@ hipError_t launch_fine_attend_t(const Geo& g, const Ws& w, const uint16_t* q, co
   const size_t shmem = Lds<D>::STAGE * sizeof(uint16_t) + 2 * kKC * sizeof(int);  // stage, index buffers
   hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(&fine_attend_kernel<D, NW>), shmem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fine_attend_kernel<D, NW>), dim3(g.fine_G, g.B * g.H), dim3(NW * 64), shmem, s,
+  const long items = (long)g.B * g.H * g.fine_G;  // below 2^31 (checked at plan time)
+  const long per_xcd = (items + kNumXcd - 1) / kNumXcd;
+  hipLaunchKernelGGL((fine_attend_kernel<D, NW>), dim3((unsigned)(per_xcd * kNumXcd)), dim3(NW * 64), shmem, s,
                      g, q, k, v, w.fine_count, w.fine_idx, o);
   return hipGetLastError();
 }

@@ -126,6 +126,9 @@ constexpr int kAmaxParts = 128;
 // Bytes of the device array that vsa_forward_noalloc uses as its workspace
 // (api.cpp): plans needing more are refused by that entry point.
 constexpr size_t kNoAllocBytes = VSA_NOALLOC_BYTES;
+// XCDs of the part: the hardware deals consecutive workgroups of a launch to
+// them in turn, and each has its own L2.
+constexpr int kNumXcd = 8;
 
 // Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
 // device, once per (device, kernel); thread-safe (api.cpp).
