@@ -64,9 +64,10 @@ def _kernel_sources(name):
 
 
 def _traffic(fragment, workload):
-    """HBM bytes per launch of the kernel whose name contains `fragment`,
-    from the committed rocprofv3 counter runs of `workload`; None when there
-    are none or the kernel's sources changed since they were taken."""
+    """HBM bytes of one attention stage: the kernels whose names contain
+    `fragment` (one launch per blocking), from the committed rocprofv3
+    counter runs of `workload`; None when there are none or a kernel's
+    sources changed since they were taken."""
     if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
@@ -74,9 +75,9 @@ def _traffic(fragment, workload):
     except (KeyError, ValueError):
         return None
     hits = [e for n, e in kernels.items() if fragment in n]
-    if len(hits) != 1 or hits[0].get("source_hash") != _src_hash(hits[0]["sources"]):
+    if not hits or any(e.get("source_hash") != _src_hash(e["sources"]) for e in hits):
         return None
-    return hits[0]["bytes_per_launch"]
+    return sum(e["bytes_per_launch"] for e in hits)
 
 
 def _short_name(name):
