@@ -271,18 +271,28 @@ int vsa_workspace_region(const vsa_plan_t* plan, int region, size_t* offset, siz
 
 /* ---- execution ----------------------------------------------------------
  * All of these enqueue kernels on `stream` and return without waiting; they
- * allocate nothing and never synchronize.  Argument errors are reported
- * before anything is enqueued; a HIP launch error returns VSA_ERR_HIP.
- * Kernel faults surface at the caller's next synchronization.  The
- * workspace (>= vsa_workspace_bytes, 256-byte aligned) is owned by the
+ * allocate no device memory and never synchronize.  Argument errors are
+ * reported before anything is enqueued; a HIP launch error returns
+ * VSA_ERR_HIP.  Kernel faults surface at the caller's next synchronization.
+ * The workspace (>= vsa_workspace_bytes, 256-byte aligned) is owned by the
  * caller and must not be shared by calls that overlap in time.
  *
- * Stream capture: the calls enqueue kernel launches only (no memset, copy
- * or allocation), so a captured graph replays them.  The first call of a
- * kernel variant in a process also raises that kernel's dynamic-LDS limit
- * (a host-side function attribute): make one uncaptured call with the plan
- * before capturing.  A replay reads the buffers captured, so new inputs go
- * into those buffers.
+ * Side streams: under a per-head blocking choice (VSA_SICS_SELECT,
+ * VSA_PROFILE_SELECT) the attention makes one launch per blocking, and the
+ * launches after the first run on library-owned streams (default priority,
+ * one set per device, made by the first uncaptured call that needs them and
+ * kept until the process ends), forked from `stream` by an event recorded on
+ * it and joined back into it before the call returns: work enqueued on
+ * `stream` afterwards waits for all of them, as for any single-stream call.
+ *
+ * Stream capture: the calls enqueue kernel launches and event records /
+ * waits only (no memset, copy or allocation), so a captured graph replays
+ * them.  The first call of a kernel variant in a process also raises that
+ * kernel's dynamic-LDS limit (a host-side function attribute) and makes the
+ * side streams: make one uncaptured call with the plan before capturing (a
+ * capture that comes first gets the blockings' launches in order on
+ * `stream`).  A replay reads the buffers captured, so new inputs go into
+ * those buffers.
  *
  * vsa_forward = vsa_layout + vsa_select + vsa_attend.  o receives the
  * attention output in the same raster layout as q. */
@@ -307,7 +317,9 @@ int vsa_forward_cached(const vsa_plan_t* plan, const void* q, const void* k, con
  * that forbid hipMalloc.  Same computation, arguments, ownership and errors
  * as vsa_forward, except that the workspace is the library's own device
  * array of VSA_NOALLOC_BYTES (256 MiB) per device, held until the process
- * ends; nothing is allocated or freed by this call.  A plan whose
+ * ends; nothing is allocated or freed by this call, and it makes no side
+ * streams (it uses a device's side streams only once another call has made
+ * them; otherwise the blockings' launches run in order on `stream`).  A plan whose
  * vsa_workspace_bytes exceeds VSA_NOALLOC_BYTES is refused with
  * VSA_ERR_UNSUPPORTED before anything is enqueued.  Every call on one device
  * shares that device's array, which keeps the previous call's contents
