@@ -29,10 +29,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
 def _src_hash(paths):
+    """Hash of the code in source files: comments and whitespace do not count
+    (a kernel is unchanged when only its comments change)."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
