@@ -59,7 +59,11 @@ SideStreams* side_streams(hipStream_t caller, bool create) {
   // Streams are made outside stream capture only: a caller that captures
   // before any uncaptured call on this device gets one stream.
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the launches' checks
+    return nullptr;
+  }
+  if (cs != hipStreamCaptureStatusNone) return nullptr;
   SideStreams* ss = new (std::nothrow) SideStreams();
   if (!ss) return nullptr;
   bool ok = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess;

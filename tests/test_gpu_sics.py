@@ -144,3 +144,28 @@ def test_wan14b_full_size():
                 assert err <= ATOL, (h, i, err)
     print(f"cand per head {cand.tolist()}, min margin {min(margins):.3e}", flush=True)
     assert set(cand[0::2].tolist()) == {1} and set(cand[1::2].tolist()) == {0}
+
+
+def test_side_streams_join_the_callers_stream():
+    """Per-head blockings launch on side streams forked from and joined into the caller's
+    stream: on a non-default stream the output equals the default stream's bit for bit, and
+    work enqueued on that stream right after the call (a copy of the output) sees all of it."""
+    wl = SMALL["sics_d128"]
+    _say("side streams on a user stream")
+    q, k, v = smooth_field_qkv(wl.B, wl.H, wl.d, wl.grid, wl.ell_per_head(), seed=2, device="cuda")
+    plan = vsa.Plan(*structs_of(wl))
+    assert plan.info.n_blockings == 3
+    ref = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    _, _, cand = plan.read_selection()
+    assert len(set(cand.tolist())) >= 2  # at least two blockings' launches in flight together
+    s = torch.cuda.Stream()
+    snaps = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            o = torch.full_like(q, 7.0)
+            plan.forward(q, k, v, o)
+            snaps.append(o.clone())
+    torch.cuda.synchronize()
+    for snap in snaps:
+        assert torch.equal(snap, ref)
