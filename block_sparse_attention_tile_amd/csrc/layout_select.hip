@@ -471,13 +471,150 @@ __device__ void bitonic_sort_blocked(double (&sv)[E], int (&si)[E], double* xs, 
   }
 }
 
+// Order-preserving key of a finite double: a larger value gives a larger
+// key, and -0 and +0 give the same key (they compare equal).
+__device__ __forceinline__ uint64_t order_key(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x + 0.0);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Exclusive prefix sum of v over the workgroup's threads in thread order;
+// *total receives the sum over all threads.  wtot: kSelThreads / 64 ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    if (w < wave) before += wtot[w];
+    all += wtot[w];
+  }
+  __syncthreads();  // wtot is reused by the next scan
+  *total = all;
+  return before + inc - v;
+}
+
+// Top-K alone (no Top-P): the K highest scores of each of the nq rows, ties
+// to the lower key tile, without sorting.  An MSB-first radix select over
+// the scores' 64-bit order keys (8-bit digits, one histogram per row in
+// LDS; lanes of a wave with the same digit add their count in one atomic)
+// finds the K-th largest key T and how many of the keys equal to T belong
+// to the top K; keys above T are kept, and the keys equal to T are kept in
+// ascending tile order up to that number.  The keys of row q are held E per
+// thread (key tile tid * E + r), as the scores were computed.
+template <int E, int QB>
+__device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq, int n, int K,
+                                           int (*hist)[256], int (*wtot)[kSelThreads / 64],
+                                           int* rdig, int* rneed, unsigned char (*keep)[kMaxTiles]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = tid * E;
+  uint64_t pre[QB];
+  int need[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    pre[q] = 0;
+    need[q] = K;
+  }
+  for (int pass = 0; pass < 8; ++pass) {
+    const int sh = 56 - 8 * pass;
+    const uint64_t hm = pass == 0 ? 0ull : (~0ull << (sh + 8));  // the digits found so far
+#pragma unroll
+    for (int q = 0; q < QB; ++q) hist[q][tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (q >= nq) break;  // uniform
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const bool m = j0 + r < n && (key[q][r] & hm) == pre[q];
+        const int dg = (int)((key[q][r] >> sh) & 255);
+        uint64_t act = __ballot(m);
+        while (act) {  // one atomic per distinct digit of the wave
+          const int leader = __ffsll((unsigned long long)act) - 1;
+          const int dl = __shfl(dg, leader);
+          const uint64_t same = __ballot(m && dg == dl);
+          if (lane == leader) atomicAdd(&hist[q][dl], __popcll(same));
+          act &= ~same;
+        }
+      }
+    }
+    __syncthreads();
+    // counts from the highest digit down: thread t holds digit 255 - t; the
+    // digit of the K-th largest is where the running count reaches need
+    int c[QB], run[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      c[q] = hist[q][255 - tid];
+      run[q] = c[q];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int t = __shfl_up(run[q], o);
+        if (lane >= o) run[q] += t;
+      }
+    if (lane == 63)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) wtot[q][wave] = run[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int w = 0; w < kSelThreads / 64; ++w)
+        if (w < wave) run[q] += wtot[q][w];
+      if (run[q] >= need[q] && run[q] - c[q] < need[q]) {
+        rdig[q] = 255 - tid;
+        rneed[q] = need[q] - (run[q] - c[q]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (q >= nq) break;
+      pre[q] |= (uint64_t)rdig[q] << sh;
+      need[q] = rneed[q];
+    }
+    // (rdig / rneed are written again only after two more barriers)
+  }
+  // pre[q]: the K-th largest key; need[q]: how many keys equal to it are kept
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if (q >= nq) break;  // uniform
+    int ties = 0;
+#pragma unroll
+    for (int r = 0; r < E; ++r) ties += (j0 + r < n && key[q][r] == pre[q]) ? 1 : 0;
+    int total;
+    int before = block_exclusive_scan(ties, wtot[0], &total);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if (j0 + r >= n) continue;
+      if (key[q][r] > pre[q]) {
+        keep[q][j0 + r] = 1;
+      } else if (key[q][r] == pre[q]) {
+        if (before < need[q]) keep[q][j0 + r] = 1;
+        ++before;
+      }
+    }
+  }
+}
+
 // One workgroup per (head, QB consecutive query tiles): window and sink flags,
 // then the block scores of every key tile against each query tile (fixed-order
 // fp64 dot products of the summaries; one pass over the key summaries serves
 // all QB query tiles), held E per thread; for Top-K / Top-P each query tile's
 // row is sorted (bitonic, mostly in registers) and its first K positions, or
-// the shortest prefix whose softmax mass reaches p, are kept; the kept flags
-// are compacted in ascending order.
+// the shortest prefix whose softmax mass reaches p, are kept (Top-K alone:
+// the K highest by a radix select, no sort); the kept flags are compacted in
+// ascending order.
 template <int E, int QB>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float* __restrict__ pooled_q,
                                                              const float* __restrict__ pooled_k,
@@ -487,7 +624,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
                                                              int* __restrict__ col_idx) {
   __shared__ unsigned char keep[QB][kMaxTiles];
   __shared__ float qbar[QB][128];
-  __shared__ int cnt[kSelThreads];
+  __shared__ int wtot_i[QB][kSelThreads / 64];
   __shared__ double wsum[kSelThreads / 64];
   __shared__ double top_s;
   extern __shared__ __align__(16) unsigned char sel_dyn[];  // exchange: double [256 E], int [256 E]
@@ -597,9 +734,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         }
       }
     }
+    if (!topp) {
+      if (K >= n) {  // every tile
+        for (int x = tid; x < nq * n; x += kSelThreads) keep[x / n][x % n] = 1;
+      } else {
+        __shared__ int rhist[QB][256];
+        __shared__ int rdig[QB], rneed[QB];
+        uint64_t key[QB][E];
+#pragma unroll
+        for (int qt = 0; qt < QB; ++qt)
+#pragma unroll
+          for (int r = 0; r < E; ++r) key[qt][r] = order_key(acc[qt][r] * g.scale);
+        topk_radix<E, QB>(key, nq, n, K, rhist, wtot_i, rdig, rneed, keep);
+      }
+    }
 #pragma unroll
     for (int qt = 0; qt < QB; ++qt) {
-      if (qt >= nq) break;  // uniform
+      if (!topp || qt >= nq) break;  // uniform
       double sv[E];
       int si[E];
 #pragma unroll
@@ -659,26 +810,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
     const int i = i0 + qt;
     int local = 0;
     for (int j = c0; j < c1; ++j) local += keep[qt][j];
-    cnt[tid] = local;
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int x = 0; x < kSelThreads; ++x) {
-        const int v = cnt[x];
-        cnt[x] = run;
-        run += v;
-      }
-      row_len[bh * g.max_tiles + i] = min(run, g.row_cap);
-    }
-    __syncthreads();
-    int pos = cnt[tid];
+    int total;
+    int pos = block_exclusive_scan(local, wtot_i[0], &total);
+    if (tid == 0) row_len[bh * g.max_tiles + i] = min(total, g.row_cap);
     int* dst = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
     for (int j = c0; j < c1; ++j)
       if (keep[qt][j]) {
         if (pos < g.row_cap) dst[pos] = j;
         ++pos;
       }
-    __syncthreads();  // cnt is reused by the next query tile
   }
 }
 
