@@ -509,20 +509,29 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int* total
 // to the top K; keys above T are kept, and the keys equal to T are kept in
 // ascending tile order up to that number.  The keys of row q are held E per
 // thread (key tile tid * E + r), as the scores were computed.
+// A row is done early when the digits found so far single out one key: that
+// key is the K-th largest, and no other key equals it.
 template <int E, int QB>
 __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq, int n, int K,
                                            int (*hist)[256], int (*wtot)[kSelThreads / 64],
-                                           int* rdig, int* rneed, unsigned char (*keep)[kMaxTiles]) {
+                                           int* rdig, int* rneed, int* rcnt, uint64_t* rkey,
+                                           unsigned char (*keep)[kMaxTiles]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = tid * E;
   uint64_t pre[QB];
   int need[QB];
+  bool done[QB];
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     pre[q] = 0;
     need[q] = K;
+    done[q] = q >= nq;
   }
   for (int pass = 0; pass < 8; ++pass) {
+    bool all_done = true;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) all_done = all_done && done[q];
+    if (all_done) break;  // uniform
     const int sh = 56 - 8 * pass;
     const uint64_t hm = pass == 0 ? 0ull : (~0ull << (sh + 8));  // the digits found so far
 #pragma unroll
@@ -530,7 +539,7 @@ __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq,
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      if (q >= nq) break;  // uniform
+      if (done[q]) continue;  // uniform
 #pragma unroll
       for (int r = 0; r < E; ++r) {
         const bool m = j0 + r < n && (key[q][r] & hm) == pre[q];
@@ -567,23 +576,41 @@ __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq,
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      if (q >= nq) break;
+      if (done[q]) continue;
 #pragma unroll
       for (int w = 0; w < kSelThreads / 64; ++w)
         if (w < wave) run[q] += wtot[q][w];
       if (run[q] >= need[q] && run[q] - c[q] < need[q]) {
         rdig[q] = 255 - tid;
         rneed[q] = need[q] - (run[q] - c[q]);
+        rcnt[q] = c[q];
       }
     }
     __syncthreads();
+    bool single = false;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      if (q >= nq) break;
+      if (done[q]) continue;
       pre[q] |= (uint64_t)rdig[q] << sh;
       need[q] = rneed[q];
+      if (rcnt[q] == 1) {  // one key left with these digits: it is the K-th largest
+        const uint64_t m = ~0ull << sh;
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+          if (j0 + r < n && (key[q][r] & m) == pre[q]) rkey[q] = key[q][r];
+        single = true;
+      }
     }
-    // (rdig / rneed are written again only after two more barriers)
+    __syncthreads();  // rkey written; rdig / rneed / rcnt read by every thread
+    if (single) {  // uniform (rcnt is read from LDS by every thread)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        if (done[q] || rcnt[q] != 1) continue;
+        pre[q] = rkey[q];
+        done[q] = true;
+      }
+      __syncthreads();  // rcnt / rkey are rewritten in the next pass
+    }
   }
   // pre[q]: the K-th largest key; need[q]: how many keys equal to it are kept
 #pragma unroll
@@ -696,19 +723,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
       // tile.  A batch of BT channels' loads is in flight before the sums,
       // which run in the fixed channel order (each fp32 x fp32 product is
       // exact in fp64).
-      constexpr int BT = E >= 8 ? 2 : 16 / E;
+      constexpr int BT = E >= 8 ? 2 : 32 / E;
       if (g.summ == VSA_SUMM_MINMAX) {
-        for (int x0 = 0; x0 < D; x0 += BT) {
-          float a[BT][E], cm[BT][E];
+        constexpr int BM = BT / 2;  // two summaries per channel
+        for (int x0 = 0; x0 < D; x0 += BM) {
+          float a[BM][E], cm[BM][E];
 #pragma unroll
-          for (int u = 0; u < BT; ++u)
+          for (int u = 0; u < BM; ++u)
 #pragma unroll
             for (int r = 0; r < E; ++r) {
               a[u][r] = kr[(long)(x0 + u) * g.max_tiles + min(j0 + r, n - 1)];
               cm[u][r] = kn[(long)(x0 + u) * g.max_tiles + min(j0 + r, n - 1)];
             }
 #pragma unroll
-          for (int u = 0; u < BT; ++u)
+          for (int u = 0; u < BM; ++u)
 #pragma unroll
             for (int qt = 0; qt < QB; ++qt) {
               const double qv = (double)qbar[qt][x0 + u];
@@ -739,13 +767,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         for (int x = tid; x < nq * n; x += kSelThreads) keep[x / n][x % n] = 1;
       } else {
         __shared__ int rhist[QB][256];
-        __shared__ int rdig[QB], rneed[QB];
+        __shared__ int rdig[QB], rneed[QB], rcnt[QB];
+        __shared__ uint64_t rkey[QB];
         uint64_t key[QB][E];
 #pragma unroll
         for (int qt = 0; qt < QB; ++qt)
 #pragma unroll
           for (int r = 0; r < E; ++r) key[qt][r] = order_key(acc[qt][r] * g.scale);
-        topk_radix<E, QB>(key, nq, n, K, rhist, wtot_i, rdig, rneed, keep);
+        topk_radix<E, QB>(key, nq, n, K, rhist, wtot_i, rdig, rneed, rcnt, rkey, keep);
       }
     }
 #pragma unroll
