@@ -515,7 +515,7 @@ template <int E, int QB>
 __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq, int n, int K,
                                            int (*hist)[256], int (*wtot)[kSelThreads / 64],
                                            int* rdig, int* rneed, int* rcnt, uint64_t* rkey,
-                                           unsigned char (*keep)[kMaxTiles]) {
+                                           unsigned char* keep, int ks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = tid * E;
   uint64_t pre[QB];
@@ -625,9 +625,9 @@ __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq,
     for (int r = 0; r < E; ++r) {
       if (j0 + r >= n) continue;
       if (key[q][r] > pre[q]) {
-        keep[q][j0 + r] = 1;
+        keep[q * ks + j0 + r] = 1;
       } else if (key[q][r] == pre[q]) {
-        if (before < need[q]) keep[q][j0 + r] = 1;
+        if (before < need[q]) keep[q * ks + j0 + r] = 1;
         ++before;
       }
     }
@@ -649,13 +649,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
                                                              const int* __restrict__ cand,
                                                              int* __restrict__ row_len,
                                                              int* __restrict__ col_idx) {
-  __shared__ unsigned char keep[QB][kMaxTiles];
+
   __shared__ float qbar[QB][128];
   __shared__ int wtot_i[QB][kSelThreads / 64];
   __shared__ double wsum[kSelThreads / 64];
   __shared__ double top_s;
-  extern __shared__ __align__(16) unsigned char sel_dyn[];  // exchange: double [256 E], int [256 E]
-  double* const xs = reinterpret_cast<double*>(sel_dyn);
+  // dynamic LDS: the kept flags [QB][ks], then (Top-P) the sort's exchange
+  // double [256 E], int [256 E]
+  extern __shared__ __align__(16) unsigned char sel_dyn[];
+  const int ks = (g.max_tiles + 15) & ~15;
+  unsigned char* const keep = sel_dyn;
+  double* const xs = reinterpret_cast<double*>(sel_dyn + QB * ks);
   int* const xi = reinterpret_cast<int*>(xs + kSelThreads * E);
 
   const int i0 = blockIdx.x * QB;
@@ -669,7 +673,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
   const int lane = tid & 63, wave = tid >> 6;
   const int D = g.d;
   const bool dense = (g.flags & VSA_DENSE) != 0;
-  for (int x = tid; x < QB * n; x += kSelThreads) keep[x / n][x % n] = (dense || x % n < g.sink) ? 1 : 0;
+  for (int x = tid; x < QB * n; x += kSelThreads) keep[(x / n) * ks + x % n] = (dense || x % n < g.sink) ? 1 : 0;
   __syncthreads();
 
   if (g.flags & VSA_WINDOW) {
@@ -695,7 +699,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         const int a0 = lo[0] + x / (e1 * e2);
         const int a1 = lo[1] + (x / e2) % e1;
         const int a2 = lo[2] + x % e2;
-        keep[qt][(a0 * b.nt[1] + a1) * b.nt[2] + a2] = 1;
+        keep[(qt) * ks + (a0 * b.nt[1] + a1) * b.nt[2] + a2] = 1;
       }
     }
   }
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
     }
     if (!topp) {
       if (K >= n) {  // every tile
-        for (int x = tid; x < nq * n; x += kSelThreads) keep[x / n][x % n] = 1;
+        for (int x = tid; x < nq * n; x += kSelThreads) keep[(x / n) * ks + x % n] = 1;
       } else {
         __shared__ int rhist[QB][256];
         __shared__ int rdig[QB], rneed[QB], rcnt[QB];
@@ -774,7 +778,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         for (int qt = 0; qt < QB; ++qt)
 #pragma unroll
           for (int r = 0; r < E; ++r) key[qt][r] = order_key(acc[qt][r] * g.scale);
-        topk_radix<E, QB>(key, nq, n, K, rhist, wtot_i, rdig, rneed, rcnt, rkey, keep);
+        topk_radix<E, QB>(key, nq, n, K, rhist, wtot_i, rdig, rneed, rcnt, rkey, keep, ks);
       }
     }
 #pragma unroll
@@ -791,7 +795,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
       bitonic_sort_blocked<E>(sv, si, xs, xi);
 #pragma unroll
       for (int r = 0; r < E; ++r)
-        if (tid * E + r < K) keep[qt][si[r]] = 1;
+        if (tid * E + r < K) keep[(qt) * ks + si[r]] = 1;
       if (topp) {
         // softmax weights in sorted order, their exclusive prefix sums (a
         // fixed-order block scan), and the shortest prefix whose mass reaches
@@ -822,7 +826,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
         double before = before_wave + inc - loc;
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-          if (si[r] < n && before / z < g.topp) keep[qt][si[r]] = 1;
+          if (si[r] < n && before / z < g.topp) keep[(qt) * ks + si[r]] = 1;
           before += e[r];
         }
         __syncthreads();  // top_s and wsum are reused by the next query tile
@@ -838,13 +842,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Geo g, const float*
   for (int qt = 0; qt < nq; ++qt) {
     const int i = i0 + qt;
     int local = 0;
-    for (int j = c0; j < c1; ++j) local += keep[qt][j];
+    for (int j = c0; j < c1; ++j) local += keep[(qt) * ks + j];
     int total;
     int pos = block_exclusive_scan(local, wtot_i[0], &total);
     if (tid == 0) row_len[bh * g.max_tiles + i] = min(total, g.row_cap);
     int* dst = col_idx + (bh * g.max_tiles + i) * (long)g.row_cap;
     for (int j = c0; j < c1; ++j)
-      if (keep[qt][j]) {
+      if (keep[(qt) * ks + j]) {
         if (pos < g.row_cap) dst[pos] = j;
         ++pos;
       }
@@ -902,7 +906,7 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
   int m = kSelThreads;
   while (m < g.max_tiles) m <<= 1;
   const int E = m / kSelThreads;
-  const size_t dyn = (size_t)m * (sizeof(double) + sizeof(int));
+  const size_t ks = ((size_t)g.max_tiles + 15) & ~(size_t)15;
   // query tiles per workgroup: 4 while the row's scores fit in registers and
   // the launch still has a few workgroups per SIMD (one pass over the key
   // summaries then serves four rows: Wan-14B selection 1.43 -> 0.90 ms), else
@@ -913,6 +917,8 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t s) {
                       : E == 8 ? select_kernel<8, 1> : select_kernel<16, 1>);
   const int qb = four ? 4 : 1;
   grid.x = (g.max_tiles + qb - 1) / qb;
+  // kept flags of the workgroup's rows; the sort's exchange only under Top-P
+  const size_t dyn = qb * ks + ((g.flags & VSA_TOPP) ? (size_t)m * (sizeof(double) + sizeof(int)) : 0);
   hipLaunchKernelGGL(kern, grid, dim3(kSelThreads), dyn, s, g, w.pooled_q, w.pooled_k, w.pooled_kmin, cand,
                      w.row_len, w.col_idx);
   return hipGetLastError();
