@@ -52,6 +52,14 @@ hipError_t ensure_dyn_lds(const void* kernel, size_t bytes) {
 SideStreams* side_streams(hipStream_t caller, bool create) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  // the set belongs to the current device: a caller's stream on another
+  // device gets the launches in order on that stream
+  hipDevice_t sdev = -1;
+  if (hipStreamGetDevice(caller, &sdev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (sdev != dev) return nullptr;
   static std::mutex mu;
   static SideStreams* made[64] = {};
   std::lock_guard<std::mutex> lock(mu);
