@@ -398,8 +398,10 @@ int build_plan(const vsa_problem* pr, const vsa_mask_policy* po, vsa_plan_s* p) 
       g.tok_cap = std::max(g.tok_cap, (long)b.n_tiles * b.slots);
     }
     // the attention launch has one workgroup per (head, tile, group of at
-    // most 12 slabs of 32 query rows): at most 11 groups per tile
-    if (BH * g.max_tiles * 11 > 0x7fffffffL)
+    // most 12 slabs of 32 query rows): at most 11 groups per tile, each
+    // head's items padded to a multiple of the 8 XCDs in the head-synchronous
+    // order
+    if (BH * ((long)g.max_tiles * 11 + 7) > 0x7fffffffL)
       return fail(VSA_ERR_UNSUPPORTED, "B*H*tiles = %ld is too large for one launch", BH * g.max_tiles);
     if (f & VSA_TOPP) {
       if (!(po->topp > 0.0 && po->topp <= 1.0))
