@@ -132,6 +132,20 @@ __device__ __forceinline__ int long_rows_first(const Geo& g, const BlkGeo& b, in
   return (co[0] * b.nt[1] + co[1]) * b.nt[2] + co[2];
 }
 
+// How many heads chose `blocking` (every head without a per-head choice).
+// Wave-uniform.
+__device__ __forceinline__ int heads_with(const Geo& g, const int* cand, int blocking) {
+  const long BH = (long)g.B * g.H;
+  if (!cand) return (int)BH;
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (long base = 0; base < BH; base += 64) {
+    const long h = base + lane;
+    n += __popcll(__ballot(h < BH && cand_of(g, cand, h) == blocking));
+  }
+  return n;
+}
+
 // The r-th head, in head order, whose chosen blocking is `blocking` (every
 // head without a per-head choice); -1 past the last.  Wave-uniform: each
 // lane tests one head of a 64-head window, a ballot counts the hits.
@@ -415,6 +429,25 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     if (bh < 0) return;
     sb = in_head % nsb;
     i0 = in_head / nsb * TPW;
+  } else if (cand) {
+    // XCD-major over the heads that chose this blocking (their count comes
+    // from the choices; the grid covers every head): each XCD takes one
+    // contiguous range of those heads' items, so the XCDs get equal shares
+    // however the choices fall.
+    const int per_head = (b.n_tiles + TPW - 1) / TPW * nsb;
+    const long n_act = (long)heads_with(g, cand, blocking) * per_head;
+    const long per_x = (n_act + kNumXcd - 1) / kNumXcd;
+    const long j = blockIdx.x / kNumXcd;
+    const long item = (blockIdx.x % kNumXcd) * per_x + j;
+    if (j >= per_x || item >= n_act) return;
+    bh = nth_head(g, cand, blocking, (int)(item / per_head));
+    if (bh < 0) return;
+    const int in_head = (int)(item % per_head);
+    sb = in_head % nsb;
+    i0 = in_head / nsb * TPW;
+    if (TPW == 1 && i0 < b.n_tiles && (g.flags & VSA_WINDOW) && g.win_mode == VSA_WIN_TRUNCATE &&
+        !(g.flags & (VSA_DENSE | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
+      i0 = long_rows_first(g, b, i0);
   } else {
     // XCD-major: each XCD takes one contiguous range of all items, so
     // neighbouring query tiles of a head (sharing window tiles) run on the
@@ -771,6 +804,10 @@ hipError_t launch_one(const Geo& g, const Ws& w, int blocking, const int* cand, 
     const long per_head = (b.n_tiles + TPW - 1) / TPW * (long)nsb;
     items = BH * per_head;
     per_xcd = (per_head + kNumXcd - 1) / kNumXcd * BH;
+  } else if (cand) {  // the chosen heads' items in eight ranges: room for every head
+    const long per_head = (b.n_tiles + TPW - 1) / TPW * (long)nsb;
+    items = BH * per_head;
+    per_xcd = (items + kNumXcd - 1) / kNumXcd;
   } else {
     items = BH * ((g.max_tiles + TPW - 1) / TPW) * nsb;
     per_xcd = (items + kNumXcd - 1) / kNumXcd;
