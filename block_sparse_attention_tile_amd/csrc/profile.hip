@@ -127,13 +127,15 @@ struct MaskedAcc {
       }
   }
 
+  // VROW: elements per V^T row of the staged chunk
+  template <int VROW>
   __device__ __forceinline__ void pv(const uint16_t* lvt, int kb, int col, int hi, const bf16x8 pb[2]) {
-    const uint16_t* vp = lvt + col * Lds<D>::VROW + kb * 32 + hi * 8;
+    const uint16_t* vp = lvt + col * VROW + kb * 32 + hi * 8;
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * VROW + half * 16);
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], acc[dt], 0, 0, 0);
       }
   }
@@ -261,6 +263,70 @@ __device__ __forceinline__ void issue_k(uint16_t* kbuf, const uint16_t* __restri
     const int c = min(u % (KC16 + 1), KC16 - 1);
     const int key = min(Lds<D>::key_of_row(p), nk - 1);
     __builtin_amdgcn_global_load_lds(k0 + (long)key * D + c * 8, (lds_ptr_t)(kbuf + ins * 512), 16, 0, 0);
+  }
+}
+
+// The masked pass stages 32-key chunks: one wave per workgroup, no sharing,
+// so a smaller stage lets more waves (and their loads) into a CU.  K rows in
+// MFMA lane order, padded like the tile kernel's (the core's score reads);
+// the K part is a whole number of 1 KB direct loads, rows past 31 are slack.
+// V^T rows hold 32 keys plus one 16-byte pad.
+template <int D>
+struct MChunk {
+  static constexpr int KC = 32;
+  static constexpr int KC16 = D / 8;
+  static constexpr int INS = (KC * (KC16 + 1) + 63) / 64;  // 1 KB direct loads of the K part
+  static constexpr int KE = INS * 512;                     // elements of the K part
+  static constexpr int VROW = KC + 8;                      // elements per V^T row
+  static constexpr int VE = D * VROW;
+};
+
+// K of keys [0, nk <= 32) by direct loads into lane-ordered rows (rows past
+// nk re-read row nk - 1), one wave.
+template <int D>
+__device__ __forceinline__ void issue_k32(uint16_t* kbuf, const uint16_t* __restrict__ k0, int nk, int lane) {
+  constexpr int INS = MChunk<D>::INS, KC16 = MChunk<D>::KC16;
+#pragma unroll
+  for (int ins = 0; ins < INS; ++ins) {
+    const int u = ins * 64 + lane;
+    const int p = u / (KC16 + 1);
+    const int c = min(u % (KC16 + 1), KC16 - 1);
+    const int key = min(Lds<D>::key_of_row(p), nk - 1);
+    __builtin_amdgcn_global_load_lds(k0 + (long)key * D + c * 8, (lds_ptr_t)(kbuf + ins * 512), 16, 0, 0);
+  }
+}
+
+// V^T of keys [0, nk <= 32) (keys past nk zero) through VGPRs: one channel
+// pair per lane (with d = 64 the two lane halves split the keys), every load
+// in flight at once, then 16-byte writes of 8 keys.
+template <int D>
+__device__ __forceinline__ void stage_v32(uint16_t* lvt, const uint16_t* __restrict__ v0, int nk, int lane) {
+  constexpr int PAIRS = D / 2;
+  static_assert(PAIRS == 64 || PAIRS == 32, "d is 64 or 128");
+  constexpr int KEYS = PAIRS == 64 ? 32 : 16;  // keys handled by one lane
+  const int pp = lane % PAIRS;
+  const int k_first = (lane / PAIRS) * KEYS;
+  uint32_t wv[KEYS];
+#pragma unroll
+  for (int j = 0; j < KEYS; ++j) {
+    const int key = k_first + j;
+    wv[j] = key < nk ? *reinterpret_cast<const uint32_t*>(v0 + (long)key * D + 2 * pp) : 0u;
+  }
+#pragma unroll
+  for (int g8 = 0; g8 < KEYS / 8; ++g8) {
+    const uint32_t* w8 = wv + g8 * 8;
+    uint4 lo, hv;
+    lo.x = (w8[0] & 0xffffu) | (w8[1] << 16);
+    lo.y = (w8[2] & 0xffffu) | (w8[3] << 16);
+    lo.z = (w8[4] & 0xffffu) | (w8[5] << 16);
+    lo.w = (w8[6] & 0xffffu) | (w8[7] << 16);
+    hv.x = (w8[0] >> 16) | (w8[1] & 0xffff0000u);
+    hv.y = (w8[2] >> 16) | (w8[3] & 0xffff0000u);
+    hv.z = (w8[4] >> 16) | (w8[5] & 0xffff0000u);
+    hv.w = (w8[6] >> 16) | (w8[7] & 0xffff0000u);
+    const int c = k_first / 8 + g8;
+    *reinterpret_cast<uint4*>(lvt + (2 * pp) * MChunk<D>::VROW + c * 8) = lo;
+    *reinterpret_cast<uint4*>(lvt + (2 * pp + 1) * MChunk<D>::VROW + c * 8) = hv;
   }
 }
 
@@ -403,7 +469,7 @@ struct MaskedChunks {
     seek(g, b, ulo, uhi);
   }
   __device__ __forceinline__ void next(const Geo& g, const BlkGeo& b, const int ulo[3], const int uhi[3]) {
-    w0 += kKC;
+    w0 += MChunk<128>::KC;
     if (w0 <= w_hi) return;
     if (++h == g.grid[1]) {
       h = 0;
@@ -411,19 +477,19 @@ struct MaskedChunks {
     }
     seek(g, b, ulo, uhi);
   }
-  __device__ __forceinline__ int keys() const { return min(kKC, w_hi + 1 - w0); }
+  __device__ __forceinline__ int keys() const { return min(MChunk<128>::KC, w_hi + 1 - w0); }
 };
 
 // One candidate (blockIdx.z) on one run: merge the full-pass segments of the
 // 32 rows, then the masked attention over the keys the candidate's static
 // mask keeps, and the sum over rows and channels of the squared difference.
 template <int D>
-__global__ __launch_bounds__(64, 1) void profile_masked_kernel(
+__global__ __launch_bounds__(64, 2) void profile_masked_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ part_acc, const float2* __restrict__ part_lm, float* __restrict__ sse) {
-  __shared__ __align__(16) uint16_t lds[Chunk<D>::KE + Lds<D>::VE];
+  __shared__ __align__(16) uint16_t lds[MChunk<D>::KE + MChunk<D>::VE];
   uint16_t* const lk = lds;
-  uint16_t* const lvt = lds + Chunk<D>::KE;
+  uint16_t* const lvt = lds + MChunk<D>::KE;
   const int run = blockIdx.x;
   const long bh = blockIdx.y;
   const int cand = blockIdx.z;
@@ -437,7 +503,56 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(
   const long head = bh * N * D;
   const BlkGeo b = pick_blk(g, cand);
 
+  core::WaveState<D> qs;  // Q fragments and the score product only
+  qs.init(q + head + qtok * D, hi);
+  MaskedAcc<D> acc;
+  acc.reset();
+  const int qt = (int)(qtok / ((long)H * W)), qh = (int)((qtok / W) % H), qw = (int)(qtok % W);
+  int blo[3], bhi[3];
+  window_axis(g, b, 0, qt, &blo[0], &bhi[0]);
+  window_axis(g, b, 1, qh, &blo[1], &bhi[1]);
+  window_axis(g, b, 2, qw, &blo[2], &bhi[2]);
+  // wave-uniform hull of the rows' boxes
+  int ulo[3], uhi[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    int lo = blo[a], hv = bhi[a];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      lo = min(lo, __shfl_xor(lo, m));
+      hv = max(hv, __shfl_xor(hv, m));
+    }
+    ulo[a] = __builtin_amdgcn_readfirstlane(lo);
+    uhi[a] = __builtin_amdgcn_readfirstlane(hv);
+  }
+  const float c2 = (float)(g.scale * 1.4426950408889634);
+
+  MaskedChunks cur;
+  for (cur.start(g, b, ulo, uhi); cur.valid; cur.next(g, b, ulo, uhi)) {
+    const int nk = cur.keys();
+    const long key0 = ((long)cur.t * H + cur.h) * W + cur.w0;
+    // this row's interval on the line (box) and the line's sink interval;
+    // a chunk that no row keeps a key of is not loaded
+    const bool in = cur.t >= blo[0] && cur.t <= bhi[0] && cur.h >= blo[1] && cur.h <= bhi[1];
+    const int ba = in ? blo[2] : 1, bb = in ? bhi[2] : 0;
+    const int lo_k = cur.w0, hi_k = lo_k + nk - 1;  // w of the chunk's keys
+    const int a1 = max(ba, lo_k), b1 = min(bb, hi_k);
+    const int a2 = lo_k, b2 = min(cur.sink_end - 1, hi_k);
+    if (!__any(a1 <= b1 || a2 <= b2)) continue;
+    __syncthreads();  // the previous chunk's reads are done
+    issue_k32<D>(lk, k + head + key0 * D, nk, lane);
+    stage_v32<D>(lvt, v + head + key0 * D, nk, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K loads have landed
+    __syncthreads();
+    f32x16 s = qs.scores(lk, 0, col, hi);
+    mask_intervals(s, a1 - lo_k, b1 - lo_k, a2 - lo_k, b2 - lo_k, hi);
+    bf16x8 pb[2];
+    acc.softmax(s, c2, pb);
+    acc.template pv<MChunk<D>::VROW>(lvt, 0, col, hi, pb);
+  }
+
   // full outputs of this lane's row and channels: merge of the segments
+  // (after the masked pass, so that their registers are free during it)
   float of[D / 32][16];
   {
     const long base = (bh * g.prof_runs + run) * g.prof_segs;
@@ -470,57 +585,6 @@ __global__ __launch_bounds__(64, 1) void profile_masked_kernel(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) of[dt][r] *= inv;
-  }
-
-  core::WaveState<D> qs;  // Q fragments and the score product only
-  qs.init(q + head + qtok * D, hi);
-  MaskedAcc<D> acc;
-  acc.reset();
-  const int qt = (int)(qtok / ((long)H * W)), qh = (int)((qtok / W) % H), qw = (int)(qtok % W);
-  int blo[3], bhi[3];
-  window_axis(g, b, 0, qt, &blo[0], &bhi[0]);
-  window_axis(g, b, 1, qh, &blo[1], &bhi[1]);
-  window_axis(g, b, 2, qw, &blo[2], &bhi[2]);
-  // wave-uniform hull of the rows' boxes
-  int ulo[3], uhi[3];
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    int lo = blo[a], hv = bhi[a];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      lo = min(lo, __shfl_xor(lo, m));
-      hv = max(hv, __shfl_xor(hv, m));
-    }
-    ulo[a] = __builtin_amdgcn_readfirstlane(lo);
-    uhi[a] = __builtin_amdgcn_readfirstlane(hv);
-  }
-  const float c2 = (float)(g.scale * 1.4426950408889634);
-
-  MaskedChunks cur;
-  for (cur.start(g, b, ulo, uhi); cur.valid; cur.next(g, b, ulo, uhi)) {
-    const int nk = cur.keys();
-    const long key0 = ((long)cur.t * H + cur.h) * W + cur.w0;
-    __syncthreads();  // the previous chunk's reads are done
-    issue_k<D>(lk, k + head + key0 * D, nk, lane);
-    stage_v_regs<D>(lvt, v + head + key0 * D, nk, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K loads have landed
-    __syncthreads();
-    // this row's interval on the line (box) and the line's sink interval
-    const bool in = cur.t >= blo[0] && cur.t <= bhi[0] && cur.h >= blo[1] && cur.h <= bhi[1];
-    const int ba = in ? blo[2] : 1, bb = in ? bhi[2] : 0;
-    for (int kb = 0; kb < 2; ++kb) {
-      const int nkb = nk - 32 * kb;
-      if (nkb <= 0) break;
-      const int lo_k = cur.w0 + 32 * kb, hi_k = lo_k + min(nkb, 32) - 1;  // w of the block's keys
-      const int a1 = max(ba, lo_k), b1 = min(bb, hi_k);
-      const int a2 = lo_k, b2 = min(cur.sink_end - 1, hi_k);
-      if (!__any(a1 <= b1 || a2 <= b2)) continue;  // no row keeps a key of this block
-      f32x16 s = qs.scores(lk, kb, col, hi);
-      mask_intervals(s, a1 - lo_k, b1 - lo_k, a2 - lo_k, b2 - lo_k, hi);
-      bf16x8 pb[2];
-      acc.softmax(s, c2, pb);
-      acc.pv(lvt, kb, col, hi, pb);
-    }
   }
 
   const float l = acc.l_part + __shfl_xor(acc.l_part, 32);
