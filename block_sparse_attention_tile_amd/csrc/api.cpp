@@ -78,7 +78,13 @@ SideStreams* side_streams(hipStream_t caller, bool create) {
   for (int i = 0; ok && i < SideStreams::kN; ++i)
     ok = hipStreamCreateWithFlags(&ss->s[i], hipStreamNonBlocking) == hipSuccess &&
          hipEventCreateWithFlags(&ss->join[i], hipEventDisableTiming) == hipSuccess;
-  if (!ok) {  // partial set-up is kept out of use (and left allocated)
+  if (!ok) {  // undo a partial set-up; the next call tries again
+    for (int i = 0; i < SideStreams::kN; ++i) {
+      if (ss->join[i]) (void)hipEventDestroy(ss->join[i]);
+      if (ss->s[i]) (void)hipStreamDestroy(ss->s[i]);
+    }
+    if (ss->fork) (void)hipEventDestroy(ss->fork);
+    delete ss;
     (void)hipGetLastError();
     return nullptr;
   }

@@ -200,8 +200,11 @@ struct ChunkIter {
 // Interleaved pair schedule (interleaved_pairs): one entry per chunk, with
 // the key tile in the low kTileBits bits, the chunk's index inside the tile
 // in the next 4, its valid keys minus one from bit kCkKeysShift (6 bits)
-// and the query-tile flags from kFlagShift.
+// and the query-tile flags from kFlagShift.  Tiles are paired only when
+// they hold at most 6 slabs (192 keys, three chunks), so the chunk index
+// fits its 4 bits.
 constexpr int kCkKeysShift = kTileBits + 4;
+static_assert(kCkKeysShift + 6 <= kFlagShift, "schedule fields do not overlap");
 
 struct ListIter {
   int c;    // position in the schedule
@@ -445,9 +448,6 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     const int in_head = (int)(item % per_head);
     sb = in_head % nsb;
     i0 = in_head / nsb * TPW;
-    if (TPW == 1 && i0 < b.n_tiles && (g.flags & VSA_WINDOW) && g.win_mode == VSA_WIN_TRUNCATE &&
-        !(g.flags & (VSA_DENSE | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
-      i0 = long_rows_first(g, b, i0);
   } else {
     // XCD-major: each XCD takes one contiguous range of all items, so
     // neighbouring query tiles of a head (sharing window tiles) run on the
@@ -460,11 +460,13 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
     i0 = ((item / nsb) % units) * TPW;  // first query tile of the workgroup
     bh = item / (nsb * units);
     if (cand_of(g, cand, bh) != blocking) return;
-    if (TPW == 1 && i0 < b.n_tiles && (g.flags & VSA_WINDOW) && g.win_mode == VSA_WIN_TRUNCATE &&
-        !(g.flags & (VSA_DENSE | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
-      i0 = long_rows_first(g, b, i0);  // (HunyuanVideo: attention 15.42 -> 15.29 ms)
   }
   if (i0 >= b.n_tiles) return;
+  // a static window truncated at the edge: longest rows first
+  // (HunyuanVideo: attention 15.42 -> 15.29 ms)
+  if (TPW == 1 && (g.flags & VSA_WINDOW) && g.win_mode == VSA_WIN_TRUNCATE &&
+      !(g.flags & (VSA_DENSE | VSA_TOPK | VSA_TOPK_FRAC | VSA_TOPP)))
+    i0 = long_rows_first(g, b, i0);
   const int slots = b.slots;
   const int q0 = sb * WPT * 32;
   if (q0 >= slots) return;

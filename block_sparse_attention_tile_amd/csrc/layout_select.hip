@@ -511,6 +511,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wtot, int* total
 // thread (key tile tid * E + r), as the scores were computed.
 // A row is done early when the digits found so far single out one key: that
 // key is the K-th largest, and no other key equals it.
+static_assert(kSelThreads == 256, "one thread per 8-bit digit");
 template <int E, int QB>
 __device__ __forceinline__ void topk_radix(const uint64_t (&key)[QB][E], int nq, int n, int K,
                                            int (*hist)[256], int (*wtot)[kSelThreads / 64],
