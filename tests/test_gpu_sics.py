@@ -169,3 +169,53 @@ def test_side_streams_join_the_callers_stream():
     torch.cuda.synchronize()
     for snap in snaps:
         assert torch.equal(snap, ref)
+
+
+def test_concurrent_callers_share_the_side_streams():
+    """Two host threads, each with its own plan, workspace and stream, call the library at the
+    same time (the binding releases the interpreter lock during each call): both plans launch
+    per-blocking work on the device's one set of side streams, and every output still equals
+    that plan's single-threaded result bit for bit."""
+    import threading
+
+    wl_a, wl_b = SMALL["sics_d128"], SMALL["sics_ragged_d64"]
+    _say("two threads, two plans, shared side streams")
+    qa, ka, va = smooth_field_qkv(wl_a.B, wl_a.H, wl_a.d, wl_a.grid, wl_a.ell_per_head(), seed=4,
+                                  device="cuda")
+    qb, kb, vb = smooth_field_qkv(wl_b.B, wl_b.H, wl_b.d, wl_b.grid, wl_b.ell_per_head(), seed=5,
+                                  device="cuda")
+    plan_a, plan_b = vsa.Plan(*structs_of(wl_a)), vsa.Plan(*structs_of(wl_b))
+    assert plan_a.info.n_blockings == 3 and plan_b.info.n_blockings == 2
+    ref_a, ref_b = plan_a.forward(qa, ka, va), plan_b.forward(qb, kb, vb)
+    torch.cuda.synchronize()
+    outs = {"a": [], "b": []}
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def worker(name, plan, q, k, v):
+        try:
+            s = torch.cuda.Stream()
+            barrier.wait()
+            with torch.cuda.stream(s):
+                for _ in range(6):
+                    o = torch.full_like(q, 3.0)
+                    plan.forward(q, k, v, o)
+                    outs[name].append(o.clone())
+            s.synchronize()
+        except Exception as e:  # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=("a", plan_a, qa, ka, va)),
+               threading.Thread(target=worker, args=("b", plan_b, qb, kb, vb))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    assert len(outs["a"]) == 6 and len(outs["b"]) == 6
+    for o in outs["a"]:
+        assert torch.equal(o, ref_a)
+    for o in outs["b"]:
+        assert torch.equal(o, ref_b)
