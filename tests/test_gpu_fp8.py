@@ -70,6 +70,12 @@ CASES = {
     "pair_units_d64": Workload("pair_units_d64", 1, 2, 64, (4, 12, 40), (2, 6, 13), topp=0.8, compute="fp8"),
     # Top-K pairs of 192-token tiles (interleaved schedule), ragged, odd tile count
     "topk_pair_ragged": Workload("topk_pair_ragged", 1, 3, 64, (7, 8, 20), (3, 8, 8), topk=4, compute="fp8"),
+    # window clamped at the grid edge (every row keeps its full window)
+    "hy_mini_clamp": Workload("hy_mini_clamp", 1, 1, 128, (12, 16, 40), (6, 8, 8), window=(1, 1, 3),
+                              win_mode="clamp", compute="fp8"),
+    # max/min bound estimator + attention sink + window + Top-P, ragged tiles, d=64
+    "topp_minmax_sink": Workload("topp_minmax_sink", 1, 3, 64, (5, 7, 9), (2, 3, 4), window=(3, 3, 3),
+                                 topp=0.9, summarizer="minmax", sink=2, compute="fp8"),
 }
 
 
