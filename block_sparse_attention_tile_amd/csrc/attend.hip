@@ -268,6 +268,7 @@ struct ChunkLoader {
 
   __device__ __forceinline__ void init(int w, int ln, int slots) {
     wave = __builtin_amdgcn_readfirstlane(w);
+    __builtin_assume(wave >= 0 && wave < NW);  // settles most per-piece branches at compile time
     lane = ln;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
@@ -303,16 +304,25 @@ struct ChunkLoader {
     return o - max(c - (HU - 1), 0) * E;
   }
 
-  __device__ __forceinline__ void issue(T* stage, const T* __restrict__ kbase,
-                                        const T* __restrict__ vbase, bool half) const {
+  template <bool HALF>
+  __device__ __forceinline__ void issue_t(T* stage, const T* __restrict__ kbase,
+                                          const T* __restrict__ vbase) const {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
       const T* base = ins < KI ? kbase : vbase;
-      __builtin_amdgcn_global_load_lds(base + (half ? off_half(x) : off_full[x]),
+      __builtin_amdgcn_global_load_lds(base + (HALF ? off_half(x) : off_full[x]),
                                        (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))), 16, 0, 0);
     }
+  }
+  // one branch per chunk on its size, not one per piece
+  __device__ __forceinline__ void issue(T* stage, const T* __restrict__ kbase,
+                                        const T* __restrict__ vbase, bool half) const {
+    if (half)
+      issue_t<true>(stage, kbase, vbase);
+    else
+      issue_t<false>(stage, kbase, vbase);
   }
 
   // Unit mode: a chunk is 64 / KU units of KU keys (16 for bf16, 32 for
@@ -326,6 +336,7 @@ struct ChunkLoader {
   __device__ __forceinline__ void init_units(int w, int ln, int slots) {
     static_assert(KU_ % E == 0, "a 16-byte V^T column lies inside one unit");
     wave = __builtin_amdgcn_readfirstlane(w);
+    __builtin_assume(wave >= 0 && wave < NW);
     lane = ln;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
