@@ -258,9 +258,12 @@ struct ChunkLoader {
   static constexpr int NI = KI + VI;
   static constexpr int PER = (NI + NW - 1) / NW;
   static_assert(KU % 64 == 0 && VU % 64 == 0, "whole instructions per part");
-  int wave;           // wave-uniform
+  static constexpr int SZ = (int)sizeof(T);
+  int wave;                // wave-uniform
   int lane;
-  int off_full[PER];  // source element offsets of this lane's pieces, 64-key chunk
+  uint32_t off_full[PER];  // source byte offsets of this lane's pieces from the chunk's K or
+                           // V^T base, 64-key chunk (a scalar base plus a 32-bit lane offset
+                           // is the load's own addressing form: no per-load address math)
 
   __device__ __forceinline__ static int ins_of(int wave, int x) {
     return min(wave + x * NW, NI - 1);  // past the last: clamped, never issued
@@ -277,12 +280,12 @@ struct ChunkLoader {
       if (ins < KI) {
         const int p = u / (L::KC16 + 1);                   // physical row
         const int c = min(u % (L::KC16 + 1), L::KC16 - 1);
-        off_full[x] = L::key_of_row(p) * D + c * E;
+        off_full[x] = (uint32_t)((L::key_of_row(p) * D + c * E) * SZ);
       } else {
         const int v = u - KU;
         const int d = v / (L::VC16 + 1);
         const int c = min(v % (L::VC16 + 1), L::VC16 - 1);
-        off_full[x] = d * slots + c * E;
+        off_full[x] = (uint32_t)((d * slots + c * E) * SZ);
       }
     }
   }
@@ -293,15 +296,15 @@ struct ChunkLoader {
   // With six or more pieces per lane, holding these offsets across the
   // loop beside the 64-key ones spills; they are recomputed per 32-key chunk
   // instead (the empty asm keeps the compiler from hoisting them).
-  __device__ __forceinline__ int off_half(int x) const {
+  __device__ __forceinline__ uint32_t off_half(int x) const {
     constexpr int HU = L::VC16 / 2;  // data units of 32 keys
-    int o = off_full[x];
+    uint32_t o = off_full[x];
     int ln = lane;
     if constexpr (PER >= 6) asm volatile("" : "+v"(o), "+v"(ln));
     const int ins = ins_of(wave, x);
-    if (ins < KI) return min(o, 31 * D + (o & (D - 1)));
+    if (ins < KI) return min(o, (uint32_t)(31 * D * SZ) + (o & (uint32_t)(D * SZ - 1)));
     const int c = min((ins * 64 + ln - KU) % (L::VC16 + 1), L::VC16 - 1);
-    return o - max(c - (HU - 1), 0) * E;
+    return o - (uint32_t)(max(c - (HU - 1), 0) * 16);  // 16 bytes per data unit
   }
 
   template <bool HALF>
@@ -311,8 +314,12 @@ struct ChunkLoader {
     for (int x = 0; x < PER; ++x) {
       if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
-      const T* base = ins < KI ? kbase : vbase;
-      __builtin_amdgcn_global_load_lds(base + (HALF ? off_half(x) : off_full[x]),
+      const char* base = reinterpret_cast<const char*>(ins < KI ? kbase : vbase);
+      uint32_t o = HALF ? off_half(x) : off_full[x];
+      // (the empty asm keeps the offset 32-bit up to the load, which then
+      // takes the scalar-base form instead of a 64-bit VGPR address)
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const T*>(base + o),
                                        (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))), 16, 0, 0);
     }
   }
@@ -346,13 +353,13 @@ struct ChunkLoader {
         const int key = L::key_of_row(u / (L::KC16 + 1));
         const int c = min(u % (L::KC16 + 1), L::KC16 - 1);
         unit_of[x] = key / KU_;
-        off_full[x] = (key % KU_) * D + c * E;
+        off_full[x] = (uint32_t)(((key % KU_) * D + c * E) * SZ);
       } else {
         const int v = u - KU;
         const int d = v / (L::VC16 + 1);
         const int c = min(v % (L::VC16 + 1), L::VC16 - 1);
         unit_of[x] = c * E / KU_;
-        off_full[x] = d * slots + (c * E) % KU_;
+        off_full[x] = (uint32_t)((d * slots + (c * E) % KU_) * SZ);
       }
     }
   }
@@ -371,9 +378,15 @@ struct ChunkLoader {
     for (int x = 0; x < PER; ++x) {
       if (wave + x * NW >= NI) break;  // wave-uniform
       const int ins = ins_of(wave, x);
-      const T* src = ins < KI ? kt_head + pick(unit_of[x], ub.k0, ub.k1, ub.k2, ub.k3)
-                              : vt_head + pick(unit_of[x], ub.v0, ub.v1, ub.v2, ub.v3);
-      __builtin_amdgcn_global_load_lds(src + off_full[x], (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))),
+      // element offsets of a head's K or V^T fit 31 bits (checked before a
+      // unit-mode launch), so the byte offset fits the 32-bit lane offset
+      const int ue = ins < KI ? pick(unit_of[x], ub.k0, ub.k1, ub.k2, ub.k3)
+                              : pick(unit_of[x], ub.v0, ub.v1, ub.v2, ub.v3);
+      const char* head = reinterpret_cast<const char*>(ins < KI ? kt_head : vt_head);
+      uint32_t o = (uint32_t)ue * (uint32_t)SZ + off_full[x];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const T*>(head + o),
+                                       (lds_ptr_t)(stage + ins * (1024 / (int)sizeof(T))),
                                        16, 0, 0);
     }
   }
