@@ -290,9 +290,10 @@ struct ChunkLoader {
     }
   }
 
-  // The source offset of piece x for a 32-key chunk: K rows past 31 and V^T
-  // key columns past 31 are clamped to the last valid ones (derived from the
-  // 64-key offset: K rows are D apart, the V^T column unit is recomputed).
+  // The source byte offset of piece x for a 32-key chunk: K rows past 31 and
+  // V^T key columns past 31 are clamped to the last valid ones (derived from
+  // the 64-key offset: K rows are D elements apart, the V^T column unit is
+  // recomputed).
   // With six or more pieces per lane, holding these offsets across the
   // loop beside the 64-key ones spills; they are recomputed per 32-key chunk
   // instead (the empty asm keeps the compiler from hoisting them).
