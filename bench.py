@@ -251,6 +251,33 @@ def _gemm_tflops(dev, stage):
     return 2.0 * 8192 ** 3 / (ms * 1e-3) / 1e12
 
 
+def _ceilings(dev, stage):
+    """Same-run practical ceilings (libvsa_ceiling.so): the attention's MFMA
+    shape (32x32x16 bf16) issued back to back at 12 waves per CU on random
+    operands that change at every product, and a plain 2 GiB HBM read
+    (best over grid sizes, with and without non-temporal loads)."""
+    import torch
+    from block_sparse_attention_tile_amd import ceiling
+    g = torch.Generator(device=dev).manual_seed(1)
+    src = torch.randn(64 * ceiling.SLICE_BYTES // 2, device=dev, dtype=torch.bfloat16, generator=g)
+    wgs, iters = 256 * 4, 3000
+    out = torch.empty(wgs * ceiling.WAVES * 64, device=dev, dtype=torch.float32)
+    flops = ceiling.mfma_bf16(src, out, wgs, iters)
+    ms = stage(lambda: ceiling.mfma_bf16(src, out, wgs, iters), 5)
+    mfma = flops / (ms * 1e-3) / 1e12
+    del src, out
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(0x5A)
+    rd = []
+    for wg in (1024, 4096, 16384):
+        o = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+        for nt in (False, True):
+            ms = stage(lambda: ceiling.read(buf, o, wg, nt), 5)
+            rd.append(buf.numel() / (ms * 1e-3) / 1e9)
+    del buf
+    return {"mfma_bf16_random_tflops": round(mfma, 1), "hbm_read_gbs": round(max(rd), 1),
+            "mfma_probe": f"{wgs} workgroups x 12 waves x {iters} x 64 products, random operands"}
+
+
 def _clamp_leg(wl, q, k, v, o, n, stage):
     """The same static workload with the window clamped at the grid edge
     (every window keeps its full 3x3x5 size: 13,500 tile pairs per head at
@@ -398,6 +425,7 @@ def main():
         clamp_leg = _clamp_leg(wl, q, k, v, o, n_st, stage)
     copy_gbs = None if wl.fine_group else _copy_gbs(dev, stage)
     gemm_tflops = None if wl.fine_group or f8 else _gemm_tflops(dev, stage)
+    ceilings = None if wl.fine_group else _ceilings(dev, stage)
 
     choice = None
     if wl.candidates:  # heads per chosen blocking (SICS or profiling selector)
@@ -443,6 +471,11 @@ def main():
         "attend_tflops": round(attn_tflops, 2),
         "gemm_bf16_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
         "attend_gemm_frac": round(attn_tflops / gemm_tflops, 4) if gemm_tflops else None,
+        "ceilings": ceilings,
+        "attend_mfma_ceiling_frac": (round(attn_tflops / ceilings["mfma_bf16_random_tflops"], 4)
+                                     if ceilings and not f8 else None),
+        "layout_read_ceiling_frac": (round(bytes_layout / (ms_layout * 1e-3) / 1e9 / ceilings["hbm_read_gbs"], 4)
+                                     if ceilings and bytes_layout else None),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "fp8": fp8_leg,

@@ -1,4 +1,5 @@
-"""Build libvsa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libvsa.so (HIP, gfx950) in-tree with hipcc, and beside it
+libvsa_ceiling.so (the same-run MFMA and HBM-read ceilings bench.py reports).
 
 Usage: python -m block_sparse_attention_tile_amd.build  (or build() from
 Python).  Always recompiles; sources are compiled in parallel.
@@ -13,11 +14,13 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvsa.so")
+CEILING_OUT = os.path.join(PKG, "libvsa_ceiling.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("VSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "layout_select.hip", "attend.hip", "sics.hip", "fine.hip", "profile.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -40,18 +43,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], CEILING_OUT)
     if verbose:
         print(f"built {OUT}")
+        print(f"built {CEILING_OUT}")
     return OUT
 
 
