@@ -252,18 +252,18 @@ def _gemm_tflops(dev, stage):
 
 
 def _ceilings(dev, stage):
-    """Same-run practical ceilings (libvsa_ceiling.so): the attention's MFMA
+    """Same-run practical ceilings (libvsa_probe.so): the attention's MFMA
     shape (32x32x16 bf16) issued back to back at 12 waves per CU on random
     operands that change at every product, and a plain 2 GiB HBM read
     (best over grid sizes, with and without non-temporal loads)."""
     import torch
-    from block_sparse_attention_tile_amd import ceiling
+    from block_sparse_attention_tile_amd import probe
     g = torch.Generator(device=dev).manual_seed(1)
-    src = torch.randn(64 * ceiling.SLICE_BYTES // 2, device=dev, dtype=torch.bfloat16, generator=g)
+    src = torch.randn(64 * probe.SLICE_BYTES // 2, device=dev, dtype=torch.bfloat16, generator=g)
     wgs, iters = 256 * 4, 3000
-    out = torch.empty(wgs * ceiling.WAVES * 64, device=dev, dtype=torch.float32)
-    flops = ceiling.mfma_bf16(src, out, wgs, iters)
-    ms = stage(lambda: ceiling.mfma_bf16(src, out, wgs, iters), 5)
+    out = torch.empty(wgs * probe.WAVES * 64, device=dev, dtype=torch.float32)
+    flops = probe.mfma_rate(src, out, wgs, iters)
+    ms = stage(lambda: probe.mfma_rate(src, out, wgs, iters), 5)
     mfma = flops / (ms * 1e-3) / 1e12
     del src, out
     buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(0x5A)
@@ -271,7 +271,7 @@ def _ceilings(dev, stage):
     for wg in (1024, 4096, 16384):
         o = torch.empty(wg * 256, dtype=torch.int32, device=dev)
         for nt in (False, True):
-            ms = stage(lambda: ceiling.read(buf, o, wg, nt), 5)
+            ms = stage(lambda: probe.read_rate(buf, o, wg, nt), 5)
             rd.append(buf.numel() / (ms * 1e-3) / 1e9)
     del buf
     return {"mfma_bf16_random_tflops": round(mfma, 1), "hbm_read_gbs": round(max(rd), 1),

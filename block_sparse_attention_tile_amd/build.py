@@ -1,5 +1,6 @@
 """Build libvsa.so (HIP, gfx950) in-tree with hipcc, and beside it
-libvsa_ceiling.so (the same-run MFMA and HBM-read ceilings bench.py reports).
+libvsa_probe.so (hardware probes: the same-run MFMA and HBM-read ceilings
+bench.py reports, and the bare E4M3 product the E4M3 parity tolerance rests on).
 
 Usage: python -m block_sparse_attention_tile_amd.build  (or build() from
 Python).  Always recompiles; sources are compiled in parallel.
@@ -14,13 +15,13 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvsa.so")
-CEILING_OUT = os.path.join(PKG, "libvsa_ceiling.so")
+PROBE_OUT = os.path.join(PKG, "libvsa_probe.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("VSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "layout_select.hip", "attend.hip", "sics.hip", "fine.hip", "profile.hip"]
-CEILING_SOURCES = ["ceiling.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -54,14 +55,14 @@ def _link(objs, out: str) -> None:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + CEILING_SOURCES
+    srcs = SOURCES + PROBE_SOURCES
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     _link(objs[:len(SOURCES)], OUT)
-    _link(objs[len(SOURCES):], CEILING_OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     if verbose:
         print(f"built {OUT}")
-        print(f"built {CEILING_OUT}")
+        print(f"built {PROBE_OUT}")
     return OUT
 
 

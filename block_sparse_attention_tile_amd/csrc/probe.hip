@@ -1,6 +1,6 @@
-// Same-run ceilings of this part (gfx950): the matrix cores with
-// data-dependent operands, and HBM reads.  Measurement only; nothing of the
-// attention method is computed here.
+// Hardware probes of this part (gfx950): the matrix cores' rate with
+// data-dependent operands, the HBM read rate, and one bare E4M3 product.
+// Measurement only; nothing of the attention method is computed here.
 //
 // The MFMA probe issues the attention kernel's product shape
 // (v_mfma_f32_32x32x16_bf16) back to back at the attention kernel's
@@ -8,19 +8,22 @@
 // one product to the next, so the matrix pipes' switching activity, and
 // with it the power-limited clock, is that of real data rather than of
 // constant registers.  The read probe streams a buffer once with 16-byte
-// loads.
+// loads.  The E4M3 probe issues the E4M3 attention's score product
+// (v_mfma_f32_32x32x64_f8f6f4) once on caller data, so a test can measure
+// its summation error against exact sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/vsa_ceiling.h"
+#include "../../include/vsa_probe.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = VSA_CEILING_WAVES;
+constexpr int kWaves = VSA_PROBE_WAVES;
 constexpr int kSliceUnits = 16 * 64;  // 16-byte units of one wave's 16 fragments
 
 __global__ __launch_bounds__(kWaves * 64, 3) void mfma_chain_kernel(const uint4* __restrict__ src,
@@ -82,12 +85,33 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   out[t] = x;
 }
 
+// Lane layout of the 32x32x64 E4M3 product: row m of A (column n of B)
+// sits in lane m (n) % 32, whose 32 bytes cover k = 32 * (lane / 32) ..
+// +31; output register r of lane (n, h) holds row 8 * (r / 4) + 4h + r % 4
+// of column n.
+__global__ __launch_bounds__(64) void mfma_f8_kernel(const uint8_t* __restrict__ a,
+                                                     const uint8_t* __restrict__ b,
+                                                     float* __restrict__ d) {
+  const int lane = threadIdx.x;
+  const int m = lane & 31, h = lane >> 5;
+  const long p = blockIdx.x;
+  const i32x8 fa = *reinterpret_cast<const i32x8*>(a + p * 2048 + m * 64 + h * 32);
+  const i32x8 fb = *reinterpret_cast<const i32x8*>(b + p * 2048 + m * 64 + h * 32);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // format 0 (E4M3) for both operands; zero scale operands: unscaled
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) d[p * 1024 + (8 * (r >> 2) + 4 * h + (r & 3)) * 32 + m] = acc[r];
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-extern "C" int vsa_ceiling_mfma_bf16(const void* src, size_t src_bytes, float* out, int workgroups,
-                                     int iters, void* stream) {
+extern "C" int vsa_probe_mfma_rate(const void* src, size_t src_bytes, float* out, int workgroups,
+                                   int iters, void* stream) {
   if (!src || !out || !aligned16(src) || !aligned16(out) || src_bytes == 0 ||
       src_bytes % (kSliceUnits * 16) != 0 || workgroups <= 0 || iters <= 0)
     return 1;
@@ -97,8 +121,8 @@ extern "C" int vsa_ceiling_mfma_bf16(const void* src, size_t src_bytes, float* o
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-extern "C" int vsa_ceiling_read(const void* src, size_t bytes, uint32_t* out, int workgroups,
-                                int nontemporal, void* stream) {
+extern "C" int vsa_probe_read_rate(const void* src, size_t bytes, uint32_t* out, int workgroups,
+                                   int nontemporal, void* stream) {
   if (!src || !out || !aligned16(src) || bytes == 0 || bytes % 16 != 0 || workgroups <= 0) return 1;
   if (nontemporal)
     hipLaunchKernelGGL(read_kernel<true>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
@@ -106,5 +130,11 @@ extern "C" int vsa_ceiling_read(const void* src, size_t bytes, uint32_t* out, in
   else
     hipLaunchKernelGGL(read_kernel<false>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const u32x4*>(src), (long)(bytes / 16), out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int vsa_probe_mfma_f8(const uint8_t* a, const uint8_t* b, float* d, int n, void* stream) {
+  if (!a || !b || !d || !aligned16(a) || !aligned16(b) || n <= 0) return 1;
+  hipLaunchKernelGGL(mfma_f8_kernel, dim3(n), dim3(64), 0, (hipStream_t)stream, a, b, d);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -9,6 +9,12 @@ from oracle import attention, fine, geometry, select, sics
 
 from block_sparse_attention_tile_amd.workload import flags_of, plan_structs as structs_of  # noqa: E402,F401
 
+# Summation error of one E4M3 matrix product (v_mfma_f32_32x32x64_f8f6f4) per
+# output element, as a fraction of its largest |term|: the bound the E4M3
+# attention's parity tolerance is derived from, measured on the hardware by
+# tests/test_gpu_probe.py.
+C_MFMA = 2.0 ** -10
+
 
 def oracle_tile_rows(wl, q_h, k_h, tile):
     """Oracle selection for one head: (rows, margins, members)."""

@@ -6,9 +6,10 @@ of the (slot-permuted) V^T rows, and the selection.
 Attention output, per query row, within a tolerance derived from the
 arithmetic (all terms computed from the oracle's values):
   * the E4M3 MFMA sums each 64-term product with an error of at most
-    C_MFMA = 2^-10 of its largest |term| (measured largest 2^-11.1 on
-    random, normal and probability-like operands; the accumulator input
-    itself is kept in fp32), so a score may be off by dS = C_MFMA * sum over
+    C_MFMA = 2^-10 of its largest |term| (tests/test_gpu_probe.py measures
+    the bare product against exact sums on uniform-code, normal,
+    probability-like and cancelling operands and holds it to this bound; the
+    accumulator input itself is kept in fp32), so a score may be off by dS = C_MFMA * sum over
     64-channel groups of max|q8| max|k8| (raw units), dt = dS * c2 in exp2
     units, plus 2^-20 (|t| + 16) for the fp32 rounding of c2, of the fma and
     of exp2;
@@ -40,10 +41,9 @@ import block_sparse_attention_tile_amd as vsa
 from block_sparse_attention_tile_amd import _lib
 from oracle import fp8, geometry, layout
 from synth import CONFIGS, Workload, smooth_field_qkv
-from tests.helpers import csr_rows, oracle_candidate, oracle_tile_rows, structs_of, unambiguous
+from tests.helpers import C_MFMA, csr_rows, oracle_candidate, oracle_tile_rows, structs_of, unambiguous
 
 pytestmark = pytest.mark.gpu
-C_MFMA = 2.0 ** -10
 
 CASES = {
     # HunyuanVideo tile shape (384 tokens, full 64-key chunks), static window
