@@ -188,15 +188,29 @@ struct WaveState {
 
   // O^T += V^T P^T for block kb.  Lane col reads channel row dt*32 + col,
   // keys 16*ks + 8*hi .. +7 of the 16-key step ks = 2*kb + half.
+  // The fragment reads run PV_AHEAD ahead of the MFMAs (each accumulator
+  // still takes half 0, then half 1).
+  static constexpr int PV_AHEAD = 2 * DT < 4 ? 2 * DT : 4;
   __device__ __forceinline__ void pv(const uint16_t* lvt, int kb, int col, int hi, const bf16x8 pb[2]) {
     const uint16_t* vp = lvt + col * Lds<D>::VROW + kb * 32 + hi * 8;
+    bf16x8 va[2 * DT];
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], acc[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        va[half * DT + dt] = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[half * DT + dt], pb[half], acc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PV_AHEAD, 0);
+#pragma unroll
+    for (int x = 0; x < 2 * DT - PV_AHEAD; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD, 0);
   }
 
   // One staged chunk with ck valid keys (1..64), block by block.
