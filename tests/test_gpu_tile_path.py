@@ -63,6 +63,10 @@ SMALL = {
     # the same with ragged edge tiles, an odd tile count (the last pair has one tile) and d=64
     "topk_pair_ragged": Workload("topk_pair_ragged", 1, 3, 64, (7, 8, 20), (3, 8, 8), topk=4),
     "eleven_slab_units": Workload("eleven_slab_units", 1, 2, 128, (12, 13, 24), (6, 7, 8), window=(3, 3, 3)),
+    # Top-K over 112-token tiles (four-wave workgroups, two per CU), three t tiles
+    "topk_112": Workload("topk_112", 1, 2, 128, (21, 8, 12), (7, 4, 4), topk=5),
+    # the same with ragged tiles on every axis (a 2-frame last t tile), two batches, d=64
+    "topk_112_ragged": Workload("topk_112_ragged", 2, 2, 64, (16, 9, 10), (7, 4, 4), topk_frac=0.3),
 }
 
 
