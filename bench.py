@@ -370,15 +370,17 @@ def main():
 
     # ---- timed region: exactly `steps` whole calls
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between consecutive calls gives each call's own time as well
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         plan.forward(q, k, v, o)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     print(f"[bench] {args.steps} calls: {ms:.3f} ms/call", file=sys.stderr, flush=True)
 
     # ---- per-stage times (same stream, HIP events around each stage)
@@ -448,6 +450,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(per_call[len(per_call) // 2], 4),
+        "ms_per_step_min": round(per_call[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
