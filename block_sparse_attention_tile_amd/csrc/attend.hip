@@ -733,7 +733,12 @@ __global__ __launch_bounds__(NW * 64, waves_per_simd(NW)) void attend_kernel(
         for (int u = 0; u < CPB; ++u) {
           if (c + u < total) {
             const T* lk = lds + ((c + u) % STAGES) * Stage::STAGE;
-            if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+            if (active && (TPW == 1 || ((cur.fl >> sub) & 1))) {
+              if constexpr (C::kF8)
+                ws.chunk(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+              else  // one-tile workgroups read the next block's K fragments during PV
+                ws.template chunk<TPW == 1>(lk, lk + Stage::KE, cur.keys(), c2, col, hi);
+            }
             cur.next(lst, nl);
           }
         }

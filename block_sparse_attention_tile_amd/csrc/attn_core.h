@@ -116,6 +116,29 @@ struct WaveState {
     return s;
   }
 
+  // K fragments of the next block read during a PV step (the first PRE of its DK).
+  static constexpr int PRE = DK < 4 ? DK : 4;
+
+  // scores() for a block whose first PRE K fragments were prefetched: the
+  // chain starts on them and the rest are read right after its first MFMA
+  // (the same products in the same order).
+  __device__ __forceinline__ f32x16 scores_pre(const uint16_t* lk, int kb, int col, int hi,
+                                               const bf16x8 pre[PRE]) const {
+    const uint16_t* kp = lk + (kb * 32 + col) * Lds<D>::KROW + hi * 8;
+    bf16x8 ka[DK];
+#pragma unroll
+    for (int kk = 0; kk < PRE; ++kk) ka[kk] = pre[kk];
+#pragma unroll
+    for (int kk = PRE; kk < DK; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < DK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (DK > PRE) __builtin_amdgcn_sched_group_barrier(0x100, DK - PRE, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, DK - 1, 0);
+    return s;
+  }
+
   // Keys at or past nk (< 32) of a block get -inf.  Register r holds key
   // 16*(r/8) + 8*hi + r%8, invalid when 16*(r/8) + r%8 >= nk - 8*hi; the
   // threshold is laundered through an empty asm so that the compares stay
@@ -213,16 +236,54 @@ struct WaveState {
     __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD, 0);
   }
 
-  // One staged chunk with ck valid keys (1..64), block by block.
+  // pv() that also reads the first PRE K fragments of block kn for the next
+  // scores_pre(): the V^T reads run PV_AHEAD ahead of the MFMAs as in pv(),
+  // then the K reads go out one per MFMA over the last PRE MFMAs.
+  __device__ __forceinline__ void pv_pf(const uint16_t* lvt, int kb, int col, int hi, const bf16x8 pb[2],
+                                        const uint16_t* lk, int kn, bf16x8 pre[PRE]) {
+    static_assert(PV_AHEAD >= PRE, "the K reads follow the V^T reads");
+    const uint16_t* vp = lvt + col * Lds<D>::VROW + kb * 32 + hi * 8;
+    bf16x8 va[2 * DT];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        va[half * DT + dt] = *reinterpret_cast<const bf16x8*>(vp + dt * 32 * Lds<D>::VROW + half * 16);
+    const uint16_t* kp = lk + (kn * 32 + col) * Lds<D>::KROW + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < PRE; ++kk) pre[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[half * DT + dt], pb[half], acc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PV_AHEAD, 0);
+#pragma unroll
+    for (int x = 0; x < 2 * DT - PV_AHEAD + PRE; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (PV_AHEAD > PRE) __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD - PRE, 0);
+  }
+
+  // One staged chunk with ck valid keys (1..64), block by block.  PF: block
+  // 1's first K fragments are read during block 0's PV step (the stage always
+  // holds 64 rows, so the reads stay in it for a 32-key chunk); off where the
+  // register budget has no room for them.
+  template <bool PF = true>
   __device__ __forceinline__ void chunk(const uint16_t* lk, const uint16_t* lvt, int ck, float c2,
                                         int col, int hi) {
     f32x16 s0 = scores(lk, 0, col, hi);
     if (ck < 32) mask(s0, ck, hi);
     bf16x8 p0[2];
     softmax(s0, c2, p0);
-    pv(lvt, 0, col, hi, p0);
+    bf16x8 pre[PRE];
+    if constexpr (PF)
+      pv_pf(lvt, 0, col, hi, p0, lk, 1, pre);
+    else
+      pv(lvt, 0, col, hi, p0);
     if (ck > 32) {
-      f32x16 s1 = scores(lk, 1, col, hi);
+      f32x16 s1 = PF ? scores_pre(lk, 1, col, hi, pre) : scores(lk, 1, col, hi);
       if (ck < 64) mask(s1, ck - 32, hi);
       bf16x8 p1[2];
       softmax(s1, c2, p1);
