@@ -48,13 +48,20 @@ def _check(name, st):
         raise RuntimeError(f"{name} failed with status {st}")
 
 
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
 def mfma_rate(src, out, workgroups: int, iters: int) -> float:
     """Launch the MFMA rate probe; returns the FLOPs it performs.  src: a
     device tensor of bf16 bits (a multiple of 16 KB); out: float32 device
     tensor of workgroups * 12 * 64 elements."""
     import torch
-    assert src.is_cuda and src.is_contiguous() and (src.numel() * src.element_size()) % SLICE_BYTES == 0
-    assert out.is_cuda and out.dtype == torch.float32 and out.numel() >= workgroups * WAVES * 64
+    _require(src.is_cuda and src.is_contiguous() and (src.numel() * src.element_size()) % SLICE_BYTES == 0,
+             "src: contiguous device tensor of whole 16 KB slices")
+    _require(out.is_cuda and out.dtype == torch.float32 and out.numel() >= workgroups * WAVES * 64,
+             "out: float32 device tensor of workgroups * 12 * 64 elements")
     _check("vsa_probe_mfma_rate",
            lib().vsa_probe_mfma_rate(C.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
                                      C.c_void_p(out.data_ptr()), workgroups, iters, _stream(src)))
@@ -65,8 +72,10 @@ def read_rate(src, out, workgroups: int, nontemporal: bool = False) -> int:
     """Launch the read probe over all of src; returns the bytes it reads.
     out: int32 device tensor of workgroups * 256 elements."""
     nbytes = src.numel() * src.element_size()
-    assert src.is_cuda and src.is_contiguous() and nbytes % 16 == 0
-    assert out.is_cuda and out.element_size() == 4 and out.numel() >= workgroups * 256
+    _require(src.is_cuda and src.is_contiguous() and nbytes % 16 == 0,
+             "src: contiguous device tensor of whole 16-byte units")
+    _require(out.is_cuda and out.element_size() == 4 and out.numel() >= workgroups * 256,
+             "out: 4-byte device tensor of workgroups * 256 elements")
     _check("vsa_probe_read_rate",
            lib().vsa_probe_read_rate(C.c_void_p(src.data_ptr()), nbytes, C.c_void_p(out.data_ptr()),
                                      workgroups, int(nontemporal), _stream(src)))
@@ -78,9 +87,10 @@ def mfma_f8(a, b, d) -> None:
     (rows, k); b: uint8 [n, 32, 64] (columns, k); d: float32 [n, 32, 32]."""
     import torch
     n = a.shape[0]
-    assert a.is_cuda and a.dtype == torch.uint8 and a.is_contiguous() and tuple(a.shape) == (n, 32, 64)
-    assert b.is_cuda and b.dtype == torch.uint8 and b.is_contiguous() and tuple(b.shape) == (n, 32, 64)
-    assert d.is_cuda and d.dtype == torch.float32 and d.is_contiguous() and tuple(d.shape) == (n, 32, 32)
+    for t, dt, shape, name in ((a, torch.uint8, (n, 32, 64), "a"), (b, torch.uint8, (n, 32, 64), "b"),
+                               (d, torch.float32, (n, 32, 32), "d")):
+        _require(t.is_cuda and t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shape,
+                 f"{name}: contiguous device tensor {dt} {shape}")
     _check("vsa_probe_mfma_f8",
            lib().vsa_probe_mfma_f8(C.c_void_p(a.data_ptr()), C.c_void_p(b.data_ptr()),
                                    C.c_void_p(d.data_ptr()), n, _stream(a)))

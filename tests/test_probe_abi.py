@@ -34,3 +34,15 @@ def test_probe_calls_refuse_bad_arguments():
     assert L.vsa_probe_mfma_f8(fake, fake, fake, 0, None) == 1
     assert L.vsa_probe_mfma_f8(odd, fake, fake, 1, None) == 1
     assert L.vsa_probe_mfma_f8(fake, None, fake, 1, None) == 1
+
+
+def test_probe_binding_refuses_host_tensors():
+    import pytest
+    import torch
+    with pytest.raises(ValueError):
+        probe.mfma_rate(torch.zeros(8192, dtype=torch.bfloat16), torch.zeros(768), 1, 1)
+    with pytest.raises(ValueError):
+        probe.read_rate(torch.zeros(16, dtype=torch.uint8), torch.zeros(256, dtype=torch.int32), 1)
+    with pytest.raises(ValueError):
+        z8 = torch.zeros(1, 32, 64, dtype=torch.uint8)
+        probe.mfma_f8(z8, z8, torch.zeros(1, 32, 32))
